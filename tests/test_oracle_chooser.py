@@ -1,0 +1,70 @@
+"""Pins of the plan-time split rule: the properties the rule states.
+
+"Fill the device with about two blocks per CU, capped by tile count and 32;
+single-pass direct write when batch * kv_heads already saturates": each
+property below is one clause of that sentence, checked over a sweep.
+"""
+import itertools
+
+import pytest
+
+from oracle.chooser import choose_decode_split, choose_prefill_grid
+
+
+SWEEP = list(itertools.product([1, 2, 7, 16, 33, 64, 128, 600],      # B_max
+                               [1, 2, 8, 16],                         # Hkv
+                               [1, 63, 64, 65, 512, 8192, 32768],     # s_max_kv
+                               [256, 80, 304],                        # n_cu
+                               [32, 64]))                             # block_n
+
+
+@pytest.mark.parametrize("B,Hkv,S,n_cu,bn", SWEEP)
+def test_split_rule_properties(B, Hkv, S, n_cu, bn):
+    p = choose_decode_split(B, S, Hkv, n_cu, bn)
+    n_units = B * Hkv
+    n_tiles = -(-S // bn)
+    ns, ch = p["nsplit"], p["chunk_tiles"]
+    assert 1 <= ns <= 32 and ns <= n_tiles
+    # contiguous chunks cover all tiles and none is empty at s_max
+    assert (ns - 1) * ch < n_tiles <= ns * ch
+    # never more splits than ~2 blocks/CU, the tile count or 32 ask for
+    want = -(-2 * n_cu // n_units)
+    target = max(1, min(want, n_tiles, 32))
+    assert ns <= target
+    # the chunk is the smallest one that stays within that count, so the
+    # device is filled as far as the caps allow
+    if ch > 1:
+        assert -(-n_tiles // (ch - 1)) > target
+    assert 2 * ns > target
+    if target == want and ns == target:
+        assert n_units * ns >= 2 * n_cu
+    # direct write exactly when one split results; saturation implies it
+    assert p["direct"] == (ns == 1)
+    if n_units >= 2 * n_cu:
+        assert p["direct"]
+    assert p["grid"] == n_units * ns
+
+
+def test_split_rule_named_regimes():
+    # one sequence, 8 KV heads, 32768 keys on 256 CUs: the 32 cap binds
+    p = choose_decode_split(1, 32768, 8, 256, 64)
+    assert p["nsplit"] == 32 and p["grid"] == 256 and p["chunk_keys"] == 1024
+    # 64 sequences x 8 KV heads = 512 units = 2 per CU: direct write
+    assert choose_decode_split(64, 8192, 8, 256, 64)["direct"]
+    # tile count binds for short KV
+    assert choose_decode_split(2, 128, 1, 256, 64)["nsplit"] == 2
+
+
+def test_forced_split_count():
+    p = choose_decode_split(1, 1000, 1, 256, 64, force_nsplit=3)
+    assert p["nsplit"] == 3 and p["chunk_tiles"] == 6
+    p = choose_decode_split(1, 100, 1, 256, 64, force_nsplit=7)
+    assert p["nsplit"] == 2          # only two tiles exist
+    p = choose_decode_split(1, 64 * 40, 1, 256, 64, force_nsplit=7)
+    assert p["nsplit"] == 7 and p["chunk_tiles"] == 6
+
+
+def test_prefill_grid():
+    g = choose_prefill_grid(16, 4096, 8, 32)
+    assert g["grid"] == 16 * 128 * 8
+    assert choose_prefill_grid(3, 33, 2, 32)["n_qtiles"] == 2
