@@ -1,0 +1,219 @@
+/*
+ * vattn.h — varlen grouped-query attention for MI355X (gfx950), C ABI.
+ *
+ * The library computes scaled-dot-product attention over ragged, THD-packed
+ * sequences with grouped-query heads: query head h reads KV head h / G,
+ * G = Hq / Hkv (the contiguous grouping that makes [T, Hq, D] ->
+ * [T, Hkv, G, D] a byte-conserving reshape; kernbench2 ADR commit page,
+ * "GQA via M-fold" finding). Scale is 1/sqrt(D). Causal visibility is
+ * bottom-right aligned: query i of a sequence sees key j iff
+ * j <= i + (Lk - Lq). A query row with no visible key gets O = 0 and
+ * LSE = -inf.
+ *
+ * Design points taken from the pages:
+ *  - Plan/execute split (cudnn-frontend issue #552 "frost(sdpa): THD execute
+ *    host round-trip", Proposal to evaluate; How the other backends avoid
+ *    this): the grid is sized at plan time from the declared B_max and s_max;
+ *    execute reads the exact cu_seqlens on the device, exits dead tiles early,
+ *    and never reads device data on the host, so a step can be captured into a
+ *    graph and nothing recompiles when lengths change.
+ *  - Split-KV decode (AstrAI commit log for csrc/kernels/gqa_decode_attn.cu,
+ *    split-KV commit): KV is partitioned across extra workgroups that emit
+ *    unnormalised (O, m, l) partials, merged by a log-sum-exp combine kernel;
+ *    the split count fills the device with about two workgroups per compute
+ *    unit, capped by the KV tile count and by 32, and falls back to one direct
+ *    write pass when batch * kv_heads already saturates the device.
+ *  - Padding mask (TransformerEngine PR #24 "[PyTorch] Build the attention
+ *    padding mask without host syncs", Description and Changes): mask =
+ *    position >= seqlen, built on the device from cu_seqlens entries 0..B.
+ *
+ * Tensor layouts (all row-major, contiguous, device memory owned by the
+ * caller; the library never allocates, frees or copies caller memory):
+ *   q, out  [T_q,  Hq,  D] bfloat16      (row t = token t of the pack)
+ *   k, v    [T_kv, Hkv, D] bfloat16
+ *   lse     [T_q,  Hq]     float32, natural log of the softmax denominator
+ *                          in units of the scaled score
+ *   cu_seqlens_q / cu_seqlens_kv  int32[>= B + 1]; sequence b owns rows
+ *                          [cu[b], cu[b+1]); entries past B are never read.
+ *
+ * Errors: host-checkable problems are reported by the return status before
+ * anything is enqueued. Problems that are only visible in device data (a
+ * length outside [0, s_max], a sequence that would run past the declared
+ * row capacity) are never reported through the status, since that would need
+ * a host read: the kernels clamp the length so that no access leaves the
+ * buffers, compute the clamped rows, and set a bit in the plan's device error
+ * word (see vattn_plan_error_word).
+ *
+ * Streams: every call that touches the device takes a hipStream_t, passed as
+ * vattn_stream_t (NULL = the legacy default stream) and enqueues on it only.
+ * Threading: a plan owns scratch memory; do not execute one plan on two
+ * streams concurrently. Different plans are independent.
+ */
+#ifndef VATTN_H
+#define VATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VATTN_ABI_VERSION 1
+
+typedef void* vattn_stream_t; /* a hipStream_t */
+
+typedef enum {
+  VATTN_OK = 0,
+  VATTN_ERR_INVALID_ARG = -1,  /* bad size, null or misaligned pointer, B > B_max */
+  VATTN_ERR_UNSUPPORTED = -2,  /* e.g. D not in {32, 64, 128, 256} */
+  VATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
+  VATTN_ERR_OOM = -4           /* plan scratch could not be allocated */
+} vattn_status;
+
+/* Bits of the device error word (sticky until vattn_plan_clear_error). */
+#define VATTN_ERRBIT_Q_LEN   0x1 /* some query length outside [0, s_max_q] was clamped */
+#define VATTN_ERRBIT_KV_LEN  0x2 /* some KV length outside [0, s_max_kv] was clamped */
+#define VATTN_ERRBIT_ROWS    0x4 /* a sequence ran past q_rows / kv_rows and was cut */
+
+typedef struct vattn_plan_s* vattn_plan_t;
+
+/* Decode compute paths. */
+#define VATTN_DECODE_AUTO 0
+#define VATTN_DECODE_WAVE 1 /* wavefront dot products + cross-lane reductions (small G) */
+#define VATTN_DECODE_MFMA 2 /* G query heads folded into the MFMA dimension */
+
+/*
+ * Plan options. Zero means "default" for every field. These serve tests and
+ * ablations; nothing is read from the environment on the hot path (the split
+ * target that the split-K blog post reads from an environment variable is a
+ * plan option here).
+ */
+typedef struct {
+  int target_blocks_per_cu; /* default 2 */
+  int nsplit_cap;           /* default 32 */
+  int force_nsplit;         /* > 0: use this split count (capped by the tile count) */
+  int force_decode_path;    /* VATTN_DECODE_* */
+  int n_cu_override;        /* > 0: plan as if the device had this many CUs */
+  int fuse_combine;         /* 1: last split workgroup of a unit merges (no 2nd launch); 2: force off */
+} vattn_plan_opts;
+
+typedef struct {
+  int B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal;
+  int is_decode;       /* 1 if s_max_q == 1 */
+  int decode_path;     /* VATTN_DECODE_WAVE or VATTN_DECODE_MFMA (decode only) */
+  int n_cu;            /* CU count the plan was sized for */
+  int block_n;         /* KV keys per tile (split granularity) */
+  int n_tiles;         /* ceil(s_max_kv / block_n) */
+  int nsplit;          /* KV splits per (sequence, kv head, head block) */
+  int chunk_keys;      /* keys per split = chunk_tiles * block_n */
+  int direct;          /* 1: one pass writes out/lse, no combine */
+  int fused_combine;   /* 1: split workgroups merge in place (no combine launch) */
+  int head_blocks;     /* decode: ceil(G / heads per workgroup) */
+  int n_units;         /* decode: B_max * Hkv * head_blocks */
+  int grid;            /* workgroups of the main kernel */
+  int combine_grid;    /* workgroups of the combine kernel (0 if none) */
+  int q_tokens_per_tile; /* prefill: query tokens per workgroup (G heads folded) */
+  int n_qtiles;        /* prefill: ceil(s_max_q / q_tokens_per_tile) */
+  int threads;         /* threads per workgroup of the main kernel */
+  long long scratch_bytes; /* device bytes owned by the plan */
+} vattn_plan_info;
+
+/* Human-readable name of a status code (static storage). */
+const char* vattn_status_string(vattn_status s);
+int vattn_abi_version(void);
+
+/*
+ * Create a plan for up to B_max sequences, query lengths <= s_max_q and KV
+ * lengths <= s_max_kv. s_max_q == 1 selects decode (split-KV + combine, or a
+ * direct pass); otherwise the causal (or full, causal = 0) varlen prefill
+ * kernel. Allowed: B_max, s_max_q, s_max_kv >= 1; Hkv >= 1; Hq % Hkv == 0;
+ * D in {32, 64, 128, 256}. The plan binds to the device current at this
+ * call, allocates its scratch (split partials, counters, error word) there
+ * once, and never allocates again. *out receives the handle.
+ */
+vattn_status vattn_plan(vattn_plan_t* out, int B_max, int s_max_q, int s_max_kv,
+                        int Hq, int Hkv, int D, int causal);
+vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_kv,
+                           int Hq, int Hkv, int D, int causal,
+                           const vattn_plan_opts* opts /* may be NULL */);
+
+/*
+ * Host-only: fill *info with the plan that vattn_plan_ex would build, without
+ * touching the device when opts->n_cu_override > 0 (otherwise the current
+ * device's CU count is queried). Allocates nothing.
+ */
+vattn_status vattn_plan_describe(int B_max, int s_max_q, int s_max_kv, int Hq,
+                                 int Hkv, int D, int causal,
+                                 const vattn_plan_opts* opts, vattn_plan_info* info);
+
+/* The chosen plan of an existing handle. */
+vattn_status vattn_plan_query(vattn_plan_t p, vattn_plan_info* info);
+
+/*
+ * Enqueue one attention pass on `stream` for sequences 0..B-1 (B <= B_max;
+ * B = 0 is a no-op). q_rows / kv_rows are the row capacities of q/out/lse and
+ * k/v (tokens allocated); no row at or past them is read or written. The call
+ * makes no host read of device data, no allocation and no synchronisation: it
+ * enqueues one kernel (direct decode, fused split decode, prefill) or two
+ * (split decode + combine) and returns. Pointers must be 16-byte aligned
+ * (lse and cu: 4-byte). Rows of out/lse that belong to no sequence are not
+ * written.
+ */
+vattn_status vattn_execute(vattn_plan_t p, int B,
+                           const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                           void* out, float* lse,
+                           int64_t q_rows, int64_t kv_rows,
+                           vattn_stream_t stream);
+
+/*
+ * Prefill comparator that the grid-sizing question asks to be measured
+ * (cudnn-frontend issue #552, Proposal to evaluate: exact grid versus
+ * oversubscription with early exit). tile_map holds n_tiles int32 entries,
+ * each (b << 16) | q_tile listing only live query tiles, computed by the
+ * caller (e.g. on the host from the lengths); the kernel runs exactly
+ * n_tiles * Hkv workgroups. Same result as vattn_execute on a prefill plan.
+ * Entries with b >= B or q_tile out of range are skipped.
+ */
+vattn_status vattn_execute_exact_grid(vattn_plan_t p, int B,
+                                      const void* q, const void* k, const void* v,
+                                      const int32_t* cu_seqlens_q,
+                                      const int32_t* cu_seqlens_kv,
+                                      void* out, float* lse,
+                                      int64_t q_rows, int64_t kv_rows,
+                                      const int32_t* tile_map, int n_tiles,
+                                      vattn_stream_t stream);
+
+/*
+ * Padding mask (TransformerEngine PR #24): for b < B and p < max_seqlen,
+ * mask[b * max_seqlen + p] = (p >= cu[b+1] - cu[b]) as a 0/1 byte (the
+ * layout of a [B, 1, 1, max_seqlen] torch.bool tensor; 1 = padded). The
+ * difference is taken in int32 with wraparound. Any int32 values are valid
+ * input: a length above max_seqlen gives an all-0 row, a negative one an
+ * all-1 row. Entries past cu[B] are never read. B = 0 is a no-op.
+ */
+vattn_status vattn_padding_mask(const int32_t* cu_seqlens, int B, int max_seqlen,
+                                uint8_t* mask, vattn_stream_t stream);
+
+/*
+ * Device address of the plan's int32 error word (VATTN_ERRBIT_*). The caller
+ * reads it after its own synchronisation; the library never does.
+ */
+const int32_t* vattn_plan_error_word(vattn_plan_t p);
+/*
+ * Diagnostic host read of the error word: waits for the device to go idle,
+ * then copies the word to *value. Synchronising by design; never call it on a
+ * hot path or inside graph capture.
+ */
+vattn_status vattn_plan_read_error(vattn_plan_t p, int32_t* value);
+/* Enqueue a reset of the error word to 0 on `stream` (a kernel, no memset). */
+vattn_status vattn_plan_clear_error(vattn_plan_t p, vattn_stream_t stream);
+
+/* Free the plan's scratch. Safe on NULL. Work already enqueued must be done. */
+void vattn_plan_destroy(vattn_plan_t p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VATTN_H */

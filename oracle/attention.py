@@ -251,3 +251,27 @@ def causal_pairs(cu_q, cu_kv, B, causal, s_max_q=None, s_max_kv=None):
         for i in range(Lq):
             total += max(0, min(Lk, i + (Lk - Lq) + 1))
     return total
+
+
+def attend_selected(q, k, v, cu_q, cu_kv, causal, picks, scale=None):
+    """Oracle values for selected (sequence b, query index i, head h) rows only.
+
+    Same definition as attend_varlen, evaluated one row at a time so that a
+    large workload can be checked on a sample. Returns a list of
+    (row, h, O [D] fp64, LSE fp64).
+    """
+    D = q.shape[2]
+    Hq, Hkv = q.shape[1], k.shape[1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    res = []
+    for b, i, h in picks:
+        q0, Lq = int(cu_q[b]), int(cu_q[b + 1]) - int(cu_q[b])
+        k0, Lk = int(cu_kv[b]), int(cu_kv[b + 1]) - int(cu_kv[b])
+        hk = kv_head_of(h, Hq, Hkv)
+        vis = visible_keys(Lq, Lk, causal)[i:i + 1]
+        o, ls = attend_rows(np.asarray(q[q0 + i:q0 + i + 1, h, :], dtype=np.float64),
+                            np.asarray(k[k0:k0 + Lk, hk, :], dtype=np.float64),
+                            np.asarray(v[k0:k0 + Lk, hk, :], dtype=np.float64), vis, scale)
+        res.append((q0 + i, h, o[0], ls[0]))
+    return res

@@ -1,0 +1,93 @@
+"""CPU checks of the C ABI: the library builds and loads, exports every
+function include/vattn.h declares, and its host-only plan chooser equals the
+oracle's split rule; plus the pure C++ chooser test (no HIP)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from oracle.chooser import choose_decode_split, choose_prefill_grid
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vattn.h")
+
+
+def _lib():
+    from varlen_gqa_attention_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    from varlen_gqa_attention_amd._lib import EXPORTS
+    assert declared_functions() == sorted(EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "varlen_gqa_attention_amd",
+                                                                     "libvattn.so")],
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (vattn_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert L.vattn_abi_version() == 1
+
+
+SWEEP = [(B, S, Hq, Hkv) for B in (1, 2, 33, 64, 300) for S in (1, 100, 4096, 32768)
+         for Hq, Hkv in ((4, 1), (32, 8), (64, 8), (128, 8), (16, 16))]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv", SWEEP)
+@pytest.mark.parametrize("n_cu", [256, 80])
+def test_describe_equals_oracle_rule(B, S, Hq, Hkv, n_cu):
+    import varlen_gqa_attention_amd as V
+    _lib()
+    info = V.describe_plan(B, 1, S, Hq, Hkv, 128, 0, n_cu_override=n_cu)
+    units = Hkv * info["head_blocks"]
+    want = choose_decode_split(B, S, units, n_cu, info["block_n"])
+    for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
+        assert info[key] == int(want[key]), key
+    p = V.describe_plan(B, max(2, S), S, Hq, Hkv, 128, 1, n_cu_override=n_cu)
+    g = choose_prefill_grid(B, max(2, S), Hkv, p["q_tokens_per_tile"])
+    assert p["n_qtiles"] == g["n_qtiles"]
+    assert p["grid"] == 8 * -(-(B * Hkv) // 8) * g["n_qtiles"]
+
+
+@pytest.mark.parametrize("force", [1, 2, 3, 7, 32, 100])
+def test_describe_forced_split_equals_oracle(force):
+    import varlen_gqa_attention_amd as V
+    _lib()
+    info = V.describe_plan(3, 1, 4097, 16, 2, 128, 0, n_cu_override=256, force_nsplit=force)
+    want = choose_decode_split(3, 4097, 2, 256, 64, force_nsplit=force)
+    assert (info["nsplit"], info["chunk_keys"]) == (want["nsplit"], want["chunk_keys"])
+
+
+def test_describe_status_codes():
+    import varlen_gqa_attention_amd as V
+    _lib()
+    with pytest.raises(V.VattnError) as e:
+        V.describe_plan(1, 1, 64, 6, 4, 64, 0, n_cu_override=256)
+    assert e.value.status == -1
+    with pytest.raises(V.VattnError) as e:
+        V.describe_plan(1, 1, 64, 8, 2, 48, 0, n_cu_override=256)
+    assert e.value.status == -2
+
+
+def test_pure_cpp_plan_test(tmp_path):
+    src = os.path.join(ROOT, "varlen_gqa_attention_amd", "csrc")
+    exe = tmp_path / "test_plan"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-o", str(exe),
+                    os.path.join(src, "tests", "test_plan.cpp"), os.path.join(src, "plan.cpp")],
+                   check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -1,0 +1,169 @@
+"""varlen_gqa_attention_amd — varlen grouped-query attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI of libvattn.so (include/vattn.h): it checks
+tensor metadata (dtype, shape, contiguity, device) and passes data pointers
+and the current HIP stream. Every step of the computation runs in the HIP
+kernels; there is no fallback path: the first call into the library raises
+ImportError when libvattn.so has not been built.
+
+    plan = Plan(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal)
+    out, lse = plan(q, k, v, cu_seqlens_q, cu_seqlens_kv, B=B)
+    mask = padding_mask(cu_seqlens, B, max_seqlen)
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import (DECODE_AUTO, DECODE_MFMA, DECODE_WAVE, ERRBIT_KV_LEN, ERRBIT_Q_LEN,
+                   ERRBIT_ROWS, PlanInfo, PlanOpts, VattnError)
+
+
+class _LazyLib:
+    """Loads libvattn.so on first use; raises ImportError if it is missing."""
+
+    def __getattr__(self, name):
+        return getattr(_lib.load(), name)
+
+
+_LIB = _LazyLib()
+
+__all__ = ["Plan", "padding_mask", "describe_plan", "VattnError", "DECODE_AUTO",
+           "DECODE_WAVE", "DECODE_MFMA", "ERRBIT_Q_LEN", "ERRBIT_KV_LEN", "ERRBIT_ROWS"]
+
+
+def _opts(target_blocks_per_cu=0, nsplit_cap=0, force_nsplit=0, force_decode_path=0,
+          n_cu_override=0, fuse_combine=0):
+    return PlanOpts(target_blocks_per_cu, nsplit_cap, force_nsplit, force_decode_path,
+                    n_cu_override, fuse_combine)
+
+
+def describe_plan(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, **opts):
+    """Plan the library would build (host only when n_cu_override > 0)."""
+    info = PlanInfo()
+    o = _opts(**opts)
+    _lib.check(_LIB.vattn_plan_describe(B_max, s_max_q, s_max_kv, Hq, Hkv, D, int(causal),
+                                        ctypes.byref(o), ctypes.byref(info)), "vattn_plan_describe")
+    return info.as_dict()
+
+
+def _stream_of(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """A plan for up to B_max sequences (see vattn_plan in include/vattn.h)."""
+
+    def __init__(self, B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal=True, **opts):
+        self._h = ctypes.c_void_p()
+        o = _opts(**opts)
+        _lib.check(_LIB.vattn_plan_ex(ctypes.byref(self._h), B_max, s_max_q, s_max_kv, Hq, Hkv,
+                                      D, int(causal), ctypes.byref(o)), "vattn_plan")
+        info = PlanInfo()
+        _lib.check(_LIB.vattn_plan_query(self._h, ctypes.byref(info)), "vattn_plan_query")
+        self.info = info.as_dict()
+        self.B_max, self.Hq, self.Hkv, self.D = B_max, Hq, Hkv, D
+
+    # -- tensors -----------------------------------------------------------
+    def _check(self, q, k, v, cu_q, cu_kv, out, lse):
+        import torch
+        for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                            ("v", v, torch.bfloat16), ("out", out, torch.bfloat16),
+                            ("lse", lse, torch.float32), ("cu_seqlens_q", cu_q, torch.int32),
+                            ("cu_seqlens_kv", cu_kv, torch.int32)):
+            if t.dtype != dt:
+                raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if q.dim() != 3 or q.shape[1:] != (self.Hq, self.D):
+            raise ValueError(f"q must be [T_q, {self.Hq}, {self.D}], got {tuple(q.shape)}")
+        for name, t in (("k", k), ("v", v)):
+            if t.dim() != 3 or t.shape[1:] != (self.Hkv, self.D):
+                raise ValueError(f"{name} must be [T_kv, {self.Hkv}, {self.D}], got {tuple(t.shape)}")
+        if k.shape != v.shape:
+            raise ValueError("k and v must have the same shape")
+        if out.shape != q.shape or lse.shape != q.shape[:2]:
+            raise ValueError("out must match q and lse must be [T_q, Hq]")
+
+    def __call__(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, out=None, lse=None, B=None,
+                 stream=None):
+        """Enqueue attention for sequences 0..B-1 (B defaults to len(cu_q) - 1)."""
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        if B is None:
+            B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_q.numel() < B + 1 or cu_seqlens_kv.numel() < B + 1:
+            raise ValueError("cu_seqlens buffers need at least B + 1 entries")
+        self._check(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, lse)
+        _lib.check(_LIB.vattn_execute(self._h, B, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                      _ptr(cu_seqlens_kv), _ptr(out), _ptr(lse), q.shape[0],
+                                      k.shape[0], _stream_of(q, stream)), "vattn_execute")
+        return out, lse
+
+    def execute_exact_grid(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, tile_map, out, lse, B,
+                           stream=None):
+        """Prefill over an exact list of live (b << 16 | q_tile) tiles."""
+        import torch
+        self._check(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, lse)
+        if tile_map.dtype != torch.int32 or not tile_map.is_cuda or not tile_map.is_contiguous():
+            raise ValueError("tile_map must be a contiguous int32 device tensor")
+        _lib.check(_LIB.vattn_execute_exact_grid(
+            self._h, B, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+            _ptr(out), _ptr(lse), q.shape[0], k.shape[0], _ptr(tile_map), tile_map.numel(),
+            _stream_of(q, stream)), "vattn_execute_exact_grid")
+        return out, lse
+
+    # -- error word --------------------------------------------------------
+    def error_word_ptr(self):
+        return _LIB.vattn_plan_error_word(self._h)
+
+    def read_error(self):
+        """Synchronising diagnostic read of the device error word."""
+        v = ctypes.c_int32()
+        _lib.check(_LIB.vattn_plan_read_error(self._h, ctypes.byref(v)), "vattn_plan_read_error")
+        return v.value
+
+    def clear_error(self, stream=None):
+        import torch
+        s = torch.cuda.current_stream() if stream is None else stream
+        _lib.check(_LIB.vattn_plan_clear_error(self._h, ctypes.c_void_p(s.cuda_stream)),
+                   "vattn_plan_clear_error")
+
+    def close(self):
+        if self._h:
+            _LIB.vattn_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def padding_mask(cu_seqlens, B, max_seqlen, out=None, stream=None):
+    """bool [B, 1, 1, max_seqlen]: True where position >= cu[b+1] - cu[b]."""
+    import torch
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 device tensor")
+    if cu_seqlens.numel() < B + 1:
+        raise ValueError("cu_seqlens needs at least B + 1 entries")
+    if out is None:
+        out = torch.empty((B, 1, 1, max_seqlen), dtype=torch.bool, device=cu_seqlens.device)
+    if out.dtype != torch.bool or not out.is_contiguous() or out.numel() != B * max_seqlen:
+        raise ValueError("out must be a contiguous bool tensor of B * max_seqlen elements")
+    _lib.check(_LIB.vattn_padding_mask(_ptr(cu_seqlens), B, max_seqlen, _ptr(out),
+                                       _stream_of(cu_seqlens, stream)), "vattn_padding_mask")
+    return out

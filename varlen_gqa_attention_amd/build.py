@@ -1,0 +1,68 @@
+"""Build libvattn.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+    python -m varlen_gqa_attention_amd.build        # or build() from Python
+
+Every HIP source is compiled with packed-FP32 code generation turned off
+(`-Xclang -target-feature -Xclang -packed-fp32-ops`); the host pass warns that
+it does not know that feature, which is harmless.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libvattn.so")
+SOURCES = ["api.cpp", "plan.cpp", "decode.hip", "prefill.hip", "mask.hip"]
+ARCH = os.environ.get("VATTN_OFFLOAD_ARCH", "gfx950")
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def _flags():
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
+
+
+def _compile(src, hipcc):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc, *_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(x for x in (r.stderr or "").splitlines() if noise not in x)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
+    return obj, err
+
+
+def build(verbose=False):
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        results = list(ex.map(lambda s: _compile(s, hipcc), SOURCES))
+    for obj, err in results:
+        if verbose and err.strip():
+            print(err, file=sys.stderr)
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+           *[o for o, _ in results]]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,262 @@
+// C ABI of the library: plan creation (the only allocation), execute (enqueue
+// only: no host read of device data, no allocation, no synchronisation), the
+// padding mask, and plan queries. See include/vattn.h for the contract.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <cmath>
+#include <new>
+
+#include "../../include/vattn.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+struct vattn_plan_s {
+  vattn_plan_info info;
+  int device;
+  uint8_t* scratch;  // error word | (m, l) partials | O partials
+  int32_t* err;
+  float2* part_ml;
+  float* part_o;
+};
+
+namespace {
+
+vattn_status device_cu_count(int* n_cu, int* dev) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) return VATTN_ERR_HIP;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess)
+    return VATTN_ERR_HIP;
+  *n_cu = n;
+  if (dev) *dev = d;
+  return VATTN_OK;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline uintptr_t align_up(uintptr_t x, uintptr_t a) { return (x + a - 1) & ~(a - 1); }
+
+}  // namespace
+
+extern "C" {
+
+const char* vattn_status_string(vattn_status s) {
+  switch (s) {
+    case VATTN_OK: return "ok";
+    case VATTN_ERR_INVALID_ARG: return "invalid argument";
+    case VATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case VATTN_ERR_HIP: return "HIP runtime error";
+    case VATTN_ERR_OOM: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+int vattn_abi_version(void) { return VATTN_ABI_VERSION; }
+
+vattn_status vattn_plan_describe(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv, int D,
+                                 int causal, const vattn_plan_opts* opts,
+                                 vattn_plan_info* info) {
+  int n_cu = (opts && opts->n_cu_override > 0) ? opts->n_cu_override : 0;
+  if (n_cu == 0) {
+    vattn_status st = device_cu_count(&n_cu, nullptr);
+    if (st != VATTN_OK) return st;
+  }
+  return vattn::plan_compute(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, opts, n_cu, info);
+}
+
+vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_kv, int Hq,
+                           int Hkv, int D, int causal, const vattn_plan_opts* opts) {
+  if (!out) return VATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  int n_cu = 0, dev = 0;
+  vattn_status st = device_cu_count(&n_cu, &dev);
+  if (st != VATTN_OK) return st;
+  if (opts && opts->n_cu_override > 0) n_cu = opts->n_cu_override;
+  vattn_plan_info info;
+  st = vattn::plan_compute(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, opts, n_cu, &info);
+  if (st != VATTN_OK) return st;
+
+  vattn_plan_s* p = new (std::nothrow) vattn_plan_s();
+  if (!p) return VATTN_ERR_OOM;
+  p->info = info;
+  p->device = dev;
+  // layout: [0, 256) error word; then (m, l) pairs; then O partials (256-aligned)
+  uintptr_t off_ml = 256;
+  uintptr_t n_part = info.direct ? 0 : (uintptr_t)B_max * Hq * info.nsplit;
+  uintptr_t off_o = align_up(off_ml + n_part * sizeof(float2), 256);
+  uintptr_t total = off_o + n_part * (uintptr_t)D * sizeof(float);
+  p->info.scratch_bytes = (long long)total;
+  void* mem = nullptr;
+  hipError_t e = hipMalloc(&mem, total);
+  if (e != hipSuccess || !mem) {
+    (void)hipGetLastError();
+    delete p;
+    return e == hipErrorOutOfMemory ? VATTN_ERR_OOM : VATTN_ERR_HIP;
+  }
+  p->scratch = (uint8_t*)mem;
+  p->err = (int32_t*)mem;
+  p->part_ml = n_part ? (float2*)(p->scratch + off_ml) : nullptr;
+  p->part_o = n_part ? (float*)(p->scratch + off_o) : nullptr;
+  // plan creation may synchronise (it is not on the hot path): zero the
+  // error word once with a kernel, then wait for it.
+  if (vattn::launch_clear_word(p->err, nullptr) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(mem);
+    delete p;
+    return VATTN_ERR_HIP;
+  }
+  *out = p;
+  return VATTN_OK;
+}
+
+vattn_status vattn_plan(vattn_plan_t* out, int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
+                        int D, int causal) {
+  return vattn_plan_ex(out, B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, nullptr);
+}
+
+vattn_status vattn_plan_query(vattn_plan_t p, vattn_plan_info* info) {
+  if (!p || !info) return VATTN_ERR_INVALID_ARG;
+  *info = p->info;
+  return VATTN_OK;
+}
+
+static vattn_status check_exec(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
+                               const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
+                               int64_t q_rows, int64_t kv_rows) {
+  if (!p) return VATTN_ERR_INVALID_ARG;
+  if (B < 0 || B > p->info.B_max) return VATTN_ERR_INVALID_ARG;
+  if (q_rows < 0 || kv_rows < 0) return VATTN_ERR_INVALID_ARG;
+  if (q_rows > INT32_MAX || kv_rows > INT32_MAX) return VATTN_ERR_UNSUPPORTED;
+  if (B == 0) return VATTN_OK;
+  if (!q || !k || !v || !cu_q || !cu_kv || !out || !lse) return VATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return VATTN_ERR_INVALID_ARG;
+  if (!aligned(lse, 4) || !aligned(cu_q, 4) || !aligned(cu_kv, 4)) return VATTN_ERR_INVALID_ARG;
+  return VATTN_OK;
+}
+
+static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
+                        const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
+                        int64_t q_rows, int64_t kv_rows, const int32_t* tile_map, int n_map,
+                        vattn_stream_t stream) {
+  const vattn_plan_info& in = p->info;
+  const float c = (float)(1.0 / std::sqrt((double)in.D) * 1.4426950408889634);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (in.is_decode) {
+    vattn::DecodeArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.cu_q = cu_q;
+    a.cu_kv = cu_kv;
+    a.out = (uint16_t*)out;
+    a.lse = lse;
+    a.part_o = p->part_o;
+    a.part_ml = p->part_ml;
+    a.err = p->err;
+    a.B = B;
+    a.Hq = in.Hq;
+    a.Hkv = in.Hkv;
+    a.G = in.Hq / in.Hkv;
+    a.head_blocks = in.head_blocks;
+    a.nsplit = in.nsplit;
+    a.chunk_keys = in.chunk_keys;
+    a.s_max_q = in.s_max_q;
+    a.s_max_kv = in.s_max_kv;
+    a.q_rows = q_rows;
+    a.kv_rows = kv_rows;
+    a.c = c;
+    a.direct = in.direct;
+    e = vattn::launch_decode(a, in.D, in.decode_path, in.threads / 64, in.grid, in.combine_grid,
+                             st);
+  } else {
+    vattn::PrefillArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.cu_q = cu_q;
+    a.cu_kv = cu_kv;
+    a.out = (uint16_t*)out;
+    a.lse = lse;
+    a.err = p->err;
+    a.tile_map = tile_map;
+    a.n_map = n_map;
+    a.B = B;
+    a.B_max = in.B_max;
+    a.Hq = in.Hq;
+    a.Hkv = in.Hkv;
+    a.G = in.Hq / in.Hkv;
+    a.tq = in.q_tokens_per_tile;
+    a.n_qtiles = in.n_qtiles;
+    a.s_max_q = in.s_max_q;
+    a.s_max_kv = in.s_max_kv;
+    a.q_rows = q_rows;
+    a.kv_rows = kv_rows;
+    a.c = c;
+    a.causal = in.causal;
+    const int64_t grid = tile_map ? (int64_t)n_map * in.Hkv : in.grid;
+    if (grid == 0) return VATTN_OK;
+    if (grid > INT32_MAX) return VATTN_ERR_UNSUPPORTED;
+    e = vattn::launch_prefill(a, in.D, (int)grid, st);
+  }
+  return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
+}
+
+vattn_status vattn_execute(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
+                           const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
+                           int64_t q_rows, int64_t kv_rows, vattn_stream_t stream) {
+  vattn_status st = check_exec(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows);
+  if (st != VATTN_OK || B == 0) return st;
+  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, nullptr, 0, stream);
+}
+
+vattn_status vattn_execute_exact_grid(vattn_plan_t p, int B, const void* q, const void* k,
+                                      const void* v, const int32_t* cu_q, const int32_t* cu_kv,
+                                      void* out, float* lse, int64_t q_rows, int64_t kv_rows,
+                                      const int32_t* tile_map, int n_tiles,
+                                      vattn_stream_t stream) {
+  vattn_status st = check_exec(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows);
+  if (st != VATTN_OK) return st;
+  if (p->info.is_decode) return VATTN_ERR_UNSUPPORTED;
+  if (n_tiles < 0 || (n_tiles > 0 && !tile_map) || !aligned(tile_map, 4))
+    return VATTN_ERR_INVALID_ARG;
+  if (B == 0 || n_tiles == 0) return VATTN_OK;
+  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, tile_map, n_tiles, stream);
+}
+
+vattn_status vattn_padding_mask(const int32_t* cu_seqlens, int B, int max_seqlen, uint8_t* mask,
+                                vattn_stream_t stream) {
+  if (B < 0 || max_seqlen < 0) return VATTN_ERR_INVALID_ARG;
+  if (B == 0 || max_seqlen == 0) return VATTN_OK;
+  if (!cu_seqlens || !mask || !aligned(cu_seqlens, 4)) return VATTN_ERR_INVALID_ARG;
+  hipError_t e = vattn::launch_padding_mask(cu_seqlens, B, max_seqlen, mask, (hipStream_t)stream);
+  return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
+}
+
+const int32_t* vattn_plan_error_word(vattn_plan_t p) { return p ? p->err : nullptr; }
+
+vattn_status vattn_plan_read_error(vattn_plan_t p, int32_t* value) {
+  if (!p || !value) return VATTN_ERR_INVALID_ARG;
+  if (hipDeviceSynchronize() != hipSuccess) return VATTN_ERR_HIP;
+  if (hipMemcpy(value, p->err, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return VATTN_ERR_HIP;
+  return VATTN_OK;
+}
+
+vattn_status vattn_plan_clear_error(vattn_plan_t p, vattn_stream_t stream) {
+  if (!p) return VATTN_ERR_INVALID_ARG;
+  return vattn::launch_clear_word(p->err, (hipStream_t)stream) == hipSuccess ? VATTN_OK
+                                                                              : VATTN_ERR_HIP;
+}
+
+void vattn_plan_destroy(vattn_plan_t p) {
+  if (!p) return;
+  if (p->scratch) (void)hipFree(p->scratch);
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,494 @@
+// Split-KV decode for varlen GQA on gfx950, plus the log-sum-exp combine.
+//
+// Method (AstrAI commit log for csrc/kernels/gqa_decode_attn.cu, split-KV
+// commit; split-K blog post, The Context: Why Split-K Matters): the KV range
+// of each (sequence, kv head) is cut into `nsplit` contiguous chunks that run
+// on separate workgroups; each emits an unnormalised partial (O, m, l) and a
+// combine kernel merges them by log-sum-exp. With one split the same
+// workgroup normalises and writes the output directly.
+//
+// Workgroup = (sequence b, kv head hk, head block hb, split s). Its waves take
+// the 32-key tiles of the chunk round-robin, keep their own running
+// (m, l, O) state, and merge through LDS at the end, so the tile loop itself
+// has no workgroup barrier. Softmax works in base 2 on t = s * scale * log2(e)
+// (the scale folds into the exponent's FMA in fp32; Q is not rounded after
+// scaling); outputs convert back with ln 2.
+//
+// Two compute paths (dispatch between an MMA and a scalar kernel by G, as in
+// the AstrAI "dispatch_decode" commit):
+//  * MFMA: the G query heads of a KV head are the 16-wide N dimension of
+//    v_mfma_f32_16x16x32_bf16 (heads folded into the matmul dimension, the
+//    kernbench "GQA via M-fold" finding). S^T = K Q^T takes K straight from
+//    global memory as the A operand (16 contiguous bytes per lane); its
+//    output layout is reused unchanged as the P^T operand of O^T = V^T P^T,
+//    and V^T comes from a wave-private, swizzled LDS tile through the
+//    gfx950 transposed LDS read.
+//  * Wave: for small G (GEMV-shaped work) each 16-byte load lane holds 8
+//    d-values of one key; dot products use v_dot2_f32_bf16 and DPP row
+//    reductions; P V is plain FMAs.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace vattn {
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Reinterpret one 32-bit word as two bf16. The word is taken by value: this
+// hipcc miscompiles __builtin_bit_cast applied directly to an ext-vector
+// element expression (it reads element 0 whatever the index).
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
+
+// Orders a wave's LDS writes before its later LDS reads (and vice versa).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct UnitCoords {
+  int b, hk, hb, s;
+};
+
+__device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
+  int bid = blockIdx.x;
+  UnitCoords u;
+  u.s = bid % a.nsplit;
+  bid /= a.nsplit;
+  u.hb = bid % a.head_blocks;
+  bid /= a.head_blocks;
+  u.hk = bid % a.Hkv;
+  u.b = bid / a.Hkv;
+  return u;
+}
+
+// Cross-wave merge of per-wave (m, l, O) states held in LDS, then the
+// epilogue: direct (normalised bf16 out + LSE) or split partial.
+// mo: [NW][HPB][D] floats, mm / ml: [NW][HPB].
+template <int D, int NW, int HPB>
+__device__ __forceinline__ void merge_and_store(const DecodeArgs& a, const UnitCoords& u,
+                                                int qrow, int h0, int nh, const float* mo,
+                                                const float* mm, const float* ml) {
+  for (int idx = threadIdx.x; idx < nh * D; idx += NW * 64) {
+    const int h = idx / D, d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * HPB + h]);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = fast_exp2(mm[w * HPB + h] - Ms);
+      L += wt * ml[w * HPB + h];
+      O += wt * mo[(w * HPB + h) * D + d];
+    }
+    const int hq = h0 + h;
+    if (a.direct) {
+      const float val = (L > 0.f) ? O / L : 0.f;
+      __bf16 ob = (__bf16)val;
+      a.out[((int64_t)qrow * a.Hq + hq) * D + d] = __builtin_bit_cast(uint16_t, ob);
+      if (d == 0)
+        a.lse[(int64_t)qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+    } else {
+      const int64_t pidx = ((int64_t)(u.b * a.Hq + hq) * a.nsplit + u.s);
+      a.part_o[pidx * D + d] = O;
+      if (d == 0) a.part_ml[pidx] = make_float2(M, L);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;     // 32-wide k-steps of Q K^T
+  constexpr int DB = D / 16;     // 16-wide d blocks of P V
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int TILE = 32;       // keys per wave iteration
+  constexpr int DV = D / 16;     // 16-byte V loads per lane per tile
+  constexpr int HPB = 16;        // heads per workgroup
+  constexpr int STAGE_BYTES = NW * TILE * D * 2;
+  constexpr int MERGE_BYTES = NW * HPB * D * 4 + 2 * NW * HPB * 4;
+  constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+  const UnitCoords u = unit_of_block(a);
+  if (u.b >= a.B) return;
+  const Span sq = read_span(a.cu_q, u.b, a.s_max_q, a.q_rows, kErrQLen);
+  const Span sk = read_span(a.cu_kv, u.b, a.s_max_kv, a.kv_rows, kErrKvLen);
+  if (u.s == 0 && u.hb == 0 && u.hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
+  if (sq.len == 0) return;
+  const int Lk = sk.len;
+  const int kbeg = u.s * a.chunk_keys;
+  if (!a.direct && kbeg >= Lk) return;  // empty split: the combine never reads it
+  const int kend = min(kbeg + a.chunk_keys, Lk);
+  const int qrow = sq.start;
+  const int h0 = u.hk * a.G + u.hb * HPB;
+  const int nh = min(HPB, a.G - u.hb * HPB);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hl = lane & 15, g4 = lane >> 4;
+
+  // Q^T operand: lane holds Q[head hl][32 ks + 8 g4 .. +8]; absent heads are 0.
+  bf16x8 qv[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 x = {0, 0, 0, 0};
+    if (hl < nh) x = ld16(a.q + ((int64_t)qrow * a.Hq + h0 + hl) * D + 32 * ks + 8 * g4);
+    qv[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  float m = kNegInf, l = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* vst = lds + w * TILE * D * 2;
+  const int64_t kvstride = (int64_t)a.Hkv * D;
+  const uint16_t* kbase = a.k + ((int64_t)sk.start * a.Hkv + u.hk) * D;
+  const uint16_t* vbase = a.v + ((int64_t)sk.start * a.Hkv + u.hk) * D;
+  const int ntiles = (kend > kbeg) ? (kend - kbeg + TILE - 1) / TILE : 0;
+
+  auto load_tile = [&](int t, u32x4 (&kr)[2][KS], u32x4 (&vr)[DV]) {
+    const int key0 = kbeg + t * TILE;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      const int key = min(key0 + 16 * kb2 + hl, kend - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = ld16(kbase + key * kvstride + 32 * ks + 8 * g4);
+    }
+#pragma unroll
+    for (int i = 0; i < DV; ++i) {
+      const int qi = i * 64 + lane;
+      const int key = min(key0 + qi / CPR, kend - 1);
+      vr[i] = ld16(vbase + key * kvstride + 8 * (qi % CPR));
+    }
+  };
+
+  u32x4 kr[2][KS], vr[DV];
+  if (w < ntiles) load_tile(w, kr, vr);
+  for (int t = w; t < ntiles; t += NW) {
+    const int key0 = kbeg + t * TILE;
+    // stage V (row-major [key][d], swizzled) in this wave's LDS slice
+#pragma unroll
+    for (int i = 0; i < DV; ++i) {
+      const int qi = i * 64 + lane;
+      const int row = qi / CPR, c = qi % CPR;
+      *reinterpret_cast<u32x4*>(vst + row * D * 2 + swz_tr16<D>(row, c) * 16) = vr[i];
+    }
+    // S^T = K Q^T for keys [16 kb2, 16 kb2 + 16)
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      sacc[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kr[kb2][ks]), qv[ks], sacc[kb2], 0, 0, 0);
+    }
+    // prefetch the wave's next tile while this one is consumed
+    u32x4 kn[2][KS], vn[DV];
+    const bool more = t + NW < ntiles;
+    if (more) load_tile(t + NW, kn, vn);
+
+    // online softmax; lane holds keys 16 kb2 + 4 g4 + i of head hl
+    float sc[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 16 * kb2 + 4 * g4 + i;
+        const float x = (key < kend) ? sacc[kb2][i] * a.c : kNegInf;
+        sc[kb2 * 4 + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float msub = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = fast_exp2(m - msub);
+    float psum = 0.f;
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fast_exp2(sc[i] - msub);
+      psum += p[i];
+    }
+    l = l * alpha + psum;
+    m = mnew;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[i] *= alpha;
+    u32x4 pw;
+    pw[0] = pack_bf16x2(p[0], p[1]);
+    pw[1] = pack_bf16x2(p[2], p[3]);
+    pw[2] = pack_bf16x2(p[4], p[5]);
+    pw[3] = pack_bf16x2(p[6], p[7]);
+    const bf16x8 pt = __builtin_bit_cast(bf16x8, pw);
+
+    wave_lds_sync();
+    // O^T += V^T P^T; V^T operand lane: d = 16 db + hl, keys 4 g4 + j and
+    // 16 + 4 g4 + j (the key order of the P^T operand above)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 16 * db + 4 * (hl & 3);
+      const int r1 = 4 * g4 + (hl >> 2), r2 = r1 + 16;
+      const int ch = col >> 3, half = (col >> 2) & 1;
+      const bf16x4 x1 = lds_read_tr(vst + r1 * D * 2 + swz_tr16<D>(r1, ch) * 16 + half * 8);
+      const bf16x4 x2 = lds_read_tr(vst + r2 * D * 2 + swz_tr16<D>(r2, ch) * 16 + half * 8);
+      const bf16x8 vt = __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pt, o[db], 0, 0, 0);
+    }
+    wave_lds_sync();
+    if (more) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = kn[kb2][ks];
+#pragma unroll
+      for (int i = 0; i < DV; ++i) vr[i] = vn[i];
+    }
+  }
+  // l: each lane summed its own 8 keys per tile; add the four key groups
+  l += xor_lane(l, 16);
+  l += xor_lane(l, 32);
+
+  __syncthreads();  // staging area becomes the merge area
+  float* mo = reinterpret_cast<float*>(lds);
+  float* mm = mo + NW * HPB * D;
+  float* ml = mm + NW * HPB;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    *reinterpret_cast<f32x4*>(mo + (w * HPB + hl) * D + 16 * db + 4 * g4) = o[db];
+  if (g4 == 0) {
+    mm[w * HPB + hl] = m;
+    ml[w * HPB + hl] = l;
+  }
+  __syncthreads();
+  merge_and_store<D, NW, HPB>(a, u, qrow, h0, nh, mo, mm, ml);
+}
+
+// ---------------------------------------------------------------------------
+// Wave (VALU) path for small G
+// ---------------------------------------------------------------------------
+template <int D, int NW, int GM>
+__global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 8;             // lanes per key row (8 d-values each)
+  constexpr int RPI = 64 / LPR;          // key rows per load instruction
+  constexpr int TILE = (D <= 128) ? 32 : 16;
+  constexpr int NI = TILE / RPI;         // loads per tile for K and for V
+  constexpr int MERGE_FLOATS = NW * GM * D + 2 * NW * GM;
+  __shared__ __attribute__((aligned(16))) float lds[MERGE_FLOATS];
+
+  const UnitCoords u = unit_of_block(a);
+  if (u.b >= a.B) return;
+  const Span sq = read_span(a.cu_q, u.b, a.s_max_q, a.q_rows, kErrQLen);
+  const Span sk = read_span(a.cu_kv, u.b, a.s_max_kv, a.kv_rows, kErrKvLen);
+  if (u.s == 0 && u.hb == 0 && u.hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
+  if (sq.len == 0) return;
+  const int Lk = sk.len;
+  const int kbeg = u.s * a.chunk_keys;
+  if (!a.direct && kbeg >= Lk) return;
+  const int kend = min(kbeg + a.chunk_keys, Lk);
+  const int qrow = sq.start;
+  const int h0 = u.hk * a.G + u.hb * GM;
+  const int nh = min(GM, a.G - u.hb * GM);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane / LPR, c = lane % LPR;
+
+  u32x4 qw[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    qw[g] = u32x4{0, 0, 0, 0};
+    if (g < nh) qw[g] = ld16(a.q + ((int64_t)qrow * a.Hq + h0 + g) * D + 8 * c);
+  }
+  float m[GM], l[GM], o[GM][8];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
+  }
+  const int64_t kvstride = (int64_t)a.Hkv * D;
+  const uint16_t* kbase = a.k + ((int64_t)sk.start * a.Hkv + u.hk) * D + 8 * c;
+  const uint16_t* vbase = a.v + ((int64_t)sk.start * a.Hkv + u.hk) * D + 8 * c;
+  const int ntiles = (kend > kbeg) ? (kend - kbeg + TILE - 1) / TILE : 0;
+
+  auto load_tile = [&](int t, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+    const int key0 = kbeg + t * TILE;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int key = min(key0 + i * RPI + r, kend - 1);
+      kr[i] = ld16(kbase + key * kvstride);
+      vr[i] = ld16(vbase + key * kvstride);
+    }
+  };
+
+  u32x4 kr[NI], vr[NI];
+  if (w < ntiles) load_tile(w, kr, vr);
+  for (int t = w; t < ntiles; t += NW) {
+    const int key0 = kbeg + t * TILE;
+    u32x4 kn[NI], vn[NI];
+    const bool more = t + NW < ntiles;
+    if (more) load_tile(t + NW, kn, vn);
+
+    float s[NI][GM];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qw[g][j]), as_bf16x2(kr[i][j]), acc,
+                                                false);
+        s[i][g] = acc;
+      }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < GM; ++g) s[i][g] = group_sum<LPR>(s[i][g]);
+
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bool ok = key0 + i * RPI + r < kend;
+        s[i][g] = ok ? s[i][g] * a.c : kNegInf;
+        mx = fmaxf(mx, s[i][g]);
+      }
+      mx = across_groups_max<LPR>(mx);
+      const float mnew = fmaxf(m[g], mx);
+      const float msub = (mnew == kNegInf) ? 0.f : mnew;
+      const float alpha = fast_exp2(m[g] - msub);
+      m[g] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        s[i][g] = fast_exp2(s[i][g] - msub);
+        psum += s[i][g];
+      }
+      l[g] = l[g] * alpha + psum;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vf[2 * j] = bf16_lo(vr[i][j]);
+        vf[2 * j + 1] = bf16_hi(vr[i][j]);
+      }
+#pragma unroll
+      for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[g][j] = fmaf(s[i][g], vf[j], o[g][j]);
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        kr[i] = kn[i];
+        vr[i] = vn[i];
+      }
+    }
+  }
+  // add the row groups' partial sums (their m are identical)
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    l[g] = across_groups_sum<LPR>(l[g]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[g][j] = across_groups_sum<LPR>(o[g][j]);
+  }
+  float* mo = lds;
+  float* mm = mo + NW * GM * D;
+  float* ml = mm + NW * GM;
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      *reinterpret_cast<f32x4*>(mo + (w * GM + g) * D + 8 * c) =
+          f32x4{o[g][0], o[g][1], o[g][2], o[g][3]};
+      *reinterpret_cast<f32x4*>(mo + (w * GM + g) * D + 8 * c + 4) =
+          f32x4{o[g][4], o[g][5], o[g][6], o[g][7]};
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      mm[w * GM + g] = m[g];
+      ml[w * GM + g] = l[g];
+    }
+  }
+  __syncthreads();
+  merge_and_store<D, NW, GM>(a, u, qrow, h0, nh, mo, mm, ml);
+}
+
+// ---------------------------------------------------------------------------
+// LSE combine: one workgroup per (sequence, query head)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  if (b >= a.B) return;
+  const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
+  if (sq.len == 0) return;
+  const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
+  const int n_live = (sk.len + a.chunk_keys - 1) / a.chunk_keys;
+  const int64_t base = (int64_t)(b * a.Hq + h) * a.nsplit;
+  float M = kNegInf;
+  for (int s = 0; s < n_live; ++s) M = fmaxf(M, a.part_ml[base + s].x);
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < n_live; ++s) {
+      const float2 ml = a.part_ml[base + s];
+      const float wt = fast_exp2(ml.x - Ms);
+      L += wt * ml.y;
+      O += wt * a.part_o[(base + s) * D + d];
+    }
+    const float val = (L > 0.f) ? O / L : 0.f;
+    __bf16 ob = (__bf16)val;
+    a.out[((int64_t)sq.start * a.Hq + h) * D + d] = __builtin_bit_cast(uint16_t, ob);
+    if (d == 0) a.lse[(int64_t)sq.start * a.Hq + h] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
+                                  hipStream_t st) {
+  if (path == 2) {
+    if (nw == 8) decode_mfma_kernel<D, 8><<<grid, 512, 0, st>>>(a);
+    else decode_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(a);
+  } else {
+    if (nw == 8) decode_wave_kernel<D, 8, 4><<<grid, 512, 0, st>>>(a);
+    else decode_wave_kernel<D, 4, 4><<<grid, 256, 0, st>>>(a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.direct) return e;
+  decode_combine_kernel<D><<<combine_grid, D < 64 ? 64 : D, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int D, int path, int nw, int grid, int combine_grid,
+                         hipStream_t st) {
+  switch (D) {
+    case 32: return launch_decode_d<32>(a, path, nw, grid, combine_grid, st);
+    case 64: return launch_decode_d<64>(a, path, nw, grid, combine_grid, st);
+    case 128: return launch_decode_d<128>(a, path, nw, grid, combine_grid, st);
+    case 256: return launch_decode_d<256>(a, path, nw, grid, combine_grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vattn

@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vattn {
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  uint16_t* out;
+  float* lse;
+  float* part_o;    // [B_max, Hq, nsplit, D] unnormalised partial outputs
+  float2* part_ml;  // [B_max, Hq, nsplit] (m in log2 units, l)
+  int32_t* err;
+  int B, Hq, Hkv, G;
+  int head_blocks;  // workgroups per (b, hk) along the head dimension
+  int nsplit, chunk_keys;
+  int s_max_q, s_max_kv;
+  int64_t q_rows, kv_rows;
+  float c;          // softmax scale * log2(e)
+  int direct;       // 1: normalise and write out/lse; 0: write partials
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  uint16_t* out;
+  float* lse;
+  int32_t* err;
+  const int32_t* tile_map;  // exact-grid comparator only (else null)
+  int n_map;
+  int B, B_max, Hq, Hkv, G;
+  int tq;        // query tokens per workgroup (rows = G * tq <= 128)
+  int n_qtiles;  // ceil(s_max_q / tq)
+  int s_max_q, s_max_kv;
+  int64_t q_rows, kv_rows;
+  float c;
+  int causal;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, int D, int path, int nw, int grid, int combine_grid,
+                         hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st);
+hipError_t launch_padding_mask(const int32_t* cu, int B, int max_seqlen, uint8_t* mask,
+                               hipStream_t st);
+hipError_t launch_clear_word(int32_t* word, hipStream_t st);
+
+}  // namespace vattn

@@ -1,0 +1,113 @@
+// Plan-time chooser (host only).
+//
+// Split rule (AstrAI commit log for csrc/kernels/gqa_decode_attn.cu,
+// split-KV commit): choose the split count to fill the device with about two
+// workgroups per CU, capped by the KV tile count and by 32; when
+// batch * kv_heads already fills the device the rule yields one split and the
+// kernel writes the output directly with no combine pass. The count depends
+// only on plan-time values (B_max, s_max_kv, heads, CU count), so it is fixed
+// inside a captured graph (split-K blog post, The Thinking Process;
+// Assumptions and Their Validity). Grids are sized from the declared B_max
+// and s_max (cudnn-frontend issue #552, Proposal to evaluate).
+//
+// Readings where the pages leave the rule open: "about two per CU" is
+// ceil(target * n_cu / n_units) with n_units the decode workgroups per split;
+// "tile count" is ceil(s_max_kv / 64); splits are contiguous chunks of whole
+// tiles and the count is recomputed from the chunk size so that no split is
+// empty at s_max_kv.
+#include "plan.hpp"
+
+#include <stdint.h>
+
+namespace vattn {
+
+static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv, int D,
+                          int causal, const vattn_plan_opts* opts, int n_cu,
+                          vattn_plan_info* info) {
+  if (!info) return VATTN_ERR_INVALID_ARG;
+  if (B_max < 1 || s_max_q < 1 || s_max_kv < 1 || Hq < 1 || Hkv < 1 || n_cu < 1)
+    return VATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return VATTN_ERR_INVALID_ARG;
+  if (s_max_q > 65535 * 128 || B_max > (1 << 15)) return VATTN_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return VATTN_ERR_UNSUPPORTED;
+  vattn_plan_opts o = {};
+  if (opts) o = *opts;
+  const int target = o.target_blocks_per_cu > 0 ? o.target_blocks_per_cu : 2;
+  const int cap = o.nsplit_cap > 0 ? o.nsplit_cap : 32;
+  const int G = Hq / Hkv;
+
+  vattn_plan_info in = {};
+  in.B_max = B_max;
+  in.s_max_q = s_max_q;
+  in.s_max_kv = s_max_kv;
+  in.Hq = Hq;
+  in.Hkv = Hkv;
+  in.D = D;
+  in.causal = causal ? 1 : 0;
+  in.n_cu = n_cu;
+  in.is_decode = (s_max_q == 1);
+
+  if (in.is_decode) {
+    int path = o.force_decode_path;
+    if (path != VATTN_DECODE_WAVE && path != VATTN_DECODE_MFMA)
+      path = (G <= kWaveMaxG) ? VATTN_DECODE_WAVE : VATTN_DECODE_MFMA;
+    in.decode_path = path;
+    const int hpb = (path == VATTN_DECODE_MFMA) ? kDecodeMfmaHeads : kDecodeWaveHeads;
+    in.head_blocks = cdiv(G, hpb);
+    const int64_t units = (int64_t)B_max * Hkv * in.head_blocks;
+    if (units > (1 << 30)) return VATTN_ERR_UNSUPPORTED;
+    in.n_units = (int)units;
+    in.block_n = kDecodeBlockN;
+    in.n_tiles = cdiv(s_max_kv, kDecodeBlockN);
+    int nsplit;
+    if (o.force_nsplit > 0) {
+      nsplit = o.force_nsplit < in.n_tiles ? o.force_nsplit : in.n_tiles;
+    } else {
+      const int64_t want = ((int64_t)target * n_cu + in.n_units - 1) / in.n_units;
+      int64_t ns = want;
+      if (ns > in.n_tiles) ns = in.n_tiles;
+      if (ns > cap) ns = cap;
+      nsplit = ns < 1 ? 1 : (int)ns;
+    }
+    const int chunk_tiles = cdiv(in.n_tiles, nsplit);
+    nsplit = cdiv(in.n_tiles, chunk_tiles);
+    in.nsplit = nsplit;
+    in.chunk_keys = chunk_tiles * kDecodeBlockN;
+    in.direct = (nsplit == 1);
+    const int64_t grid = (int64_t)in.n_units * nsplit;
+    if (grid > (1LL << 31) - 1) return VATTN_ERR_UNSUPPORTED;
+    in.grid = (int)grid;
+    // one wave per tile of the chunk, up to 8; 8 waves when at most one
+    // workgroup lands on each CU so that a lone workgroup keeps enough bytes
+    // in flight.
+    // (D = 256 stays at 4 waves: 8 would exceed the register file.)
+    in.threads = (in.grid <= n_cu && D <= 128) ? 512 : 256;
+    in.fused_combine = 0;
+    in.combine_grid = in.direct ? 0 : B_max * Hq;
+    in.scratch_bytes = 256;  // error word, aligned
+    if (!in.direct)
+      in.scratch_bytes += (int64_t)B_max * Hq * nsplit * ((int64_t)D * 4 + 8);
+  } else {
+    if (G > kPrefillRows) return VATTN_ERR_UNSUPPORTED;
+    in.q_tokens_per_tile = kPrefillRows / G;
+    in.n_qtiles = cdiv(s_max_q, in.q_tokens_per_tile);
+    if (in.n_qtiles > 65535) return VATTN_ERR_UNSUPPORTED;
+    const int64_t units = (int64_t)B_max * Hkv;
+    const int64_t grid = 8 * ((units + 7) / 8) * (int64_t)in.n_qtiles;
+    if (grid > (1LL << 31) - 1) return VATTN_ERR_UNSUPPORTED;
+    in.n_units = (int)units;
+    in.grid = (int)grid;
+    in.threads = 256;
+    in.block_n = 64;
+    in.n_tiles = cdiv(s_max_kv, 64);
+    in.nsplit = 1;
+    in.direct = 1;
+    in.scratch_bytes = 256;
+  }
+  *info = in;
+  return VATTN_OK;
+}
+
+}  // namespace vattn

@@ -1,0 +1,20 @@
+// Plan-time chooser: pure host arithmetic, no HIP calls (unit-testable on a
+// machine without a GPU).
+#pragma once
+#include "../../include/vattn.h"
+
+namespace vattn {
+
+// Geometry fixed by the kernels.
+constexpr int kDecodeBlockN = 64;     // decode KV tile used by the split rule (keys)
+constexpr int kDecodeMfmaHeads = 16;  // heads per workgroup on the MFMA decode path
+constexpr int kDecodeWaveHeads = 4;   // heads per workgroup on the wave decode path
+constexpr int kWaveMaxG = 4;          // auto: G <= this uses the wave path
+constexpr int kPrefillRows = 128;     // query rows (heads x tokens) per prefill workgroup
+
+// Fills *info (sizes only; no allocation). n_cu must be > 0.
+vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv, int D,
+                          int causal, const vattn_plan_opts* opts, int n_cu,
+                          vattn_plan_info* info);
+
+}  // namespace vattn

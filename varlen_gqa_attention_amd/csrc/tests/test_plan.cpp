@@ -1,0 +1,57 @@
+// Host-only checks of the plan chooser (no HIP): built with the system C++
+// compiler against plan.cpp. Exits non-zero on the first failure.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <initializer_list>
+
+#include "../plan.hpp"
+
+#define CHECK(c)                                                   \
+  do {                                                             \
+    if (!(c)) {                                                    \
+      fprintf(stderr, "FAILED %s at %s:%d\n", #c, __FILE__, __LINE__); \
+      exit(1);                                                     \
+    }                                                              \
+  } while (0)
+
+static int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+int main() {
+  vattn_plan_info in;
+  // one long sequence, 8 KV heads, 256 CUs: the cap of 32 binds
+  CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.is_decode && in.nsplit == 32 && in.grid == 256 && in.chunk_keys == 1024 && !in.direct);
+  CHECK(in.decode_path == VATTN_DECODE_MFMA && in.combine_grid == 64);
+  // batch * kv heads fills the device: direct write
+  CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0 && in.decode_path == VATTN_DECODE_WAVE);
+  // prefill grid from B_max and s_max_q, G heads folded into 128 rows
+  CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 128, 1, nullptr, 256, &in) == VATTN_OK);
+  CHECK(!in.is_decode && in.q_tokens_per_tile == 32 && in.n_qtiles == 128 && in.grid == 16384);
+  // validation
+  CHECK(vattn::plan_compute(1, 1, 64, 6, 4, 64, 0, nullptr, 256, &in) == VATTN_ERR_INVALID_ARG);
+  CHECK(vattn::plan_compute(1, 1, 64, 8, 2, 80, 0, nullptr, 256, &in) == VATTN_ERR_UNSUPPORTED);
+  CHECK(vattn::plan_compute(0, 1, 64, 8, 2, 64, 0, nullptr, 256, &in) == VATTN_ERR_INVALID_ARG);
+  CHECK(vattn::plan_compute(1, 0, 64, 8, 2, 64, 0, nullptr, 256, &in) == VATTN_ERR_INVALID_ARG);
+  // sweep: split-rule invariants
+  const int Bs[] = {1, 3, 16, 64, 200}, Ss[] = {1, 64, 65, 1000, 32768}, Hs[] = {1, 2, 8};
+  for (int B : Bs)
+    for (int S : Ss)
+      for (int Hkv : Hs)
+        for (int G : {1, 4, 8, 20}) {
+          CHECK(vattn::plan_compute(B, 1, S, Hkv * G, Hkv, 64, 0, nullptr, 256, &in) == VATTN_OK);
+          const int tiles = cdiv(S, 64);
+          CHECK(in.nsplit >= 1 && in.nsplit <= 32 && in.nsplit <= tiles);
+          CHECK((in.nsplit - 1) * in.chunk_keys < tiles * 64 && in.nsplit * in.chunk_keys >= S);
+          CHECK(in.grid == in.n_units * in.nsplit);
+          CHECK(in.direct == (in.nsplit == 1));
+          if (in.n_units >= 512) CHECK(in.direct);
+        }
+  vattn_plan_opts o = {};
+  o.force_nsplit = 7;
+  CHECK(vattn::plan_compute(1, 1, 64 * 40, 8, 8, 64, 0, &o, 256, &in) == VATTN_OK);
+  CHECK(in.nsplit == 7 && in.chunk_keys == 6 * 64);
+  printf("test_plan: ok\n");
+  return 0;
+}
