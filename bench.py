@@ -1,0 +1,374 @@
+#!/usr/bin/env python3
+"""Throughput of the varlen GQA hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: long decode, B=1, Hq=64, Hkv=8 (G=8), D=128, one query
+token over 32768 keys (split-KV: 32 splits x 8 KV heads = 256 workgroups).
+A step is one execute of the plan (split kernel + merge) replayed from a
+captured HIP graph, with inputs resident in HBM. K/V rotate over enough
+copies (> 2x the 256 MB Infinity Cache) that every step reads from HBM.
+
+Prints ONE JSON line: value = KV GB/s over the K timed steps (whole job, one
+GPU), roofline of the dominant kernel (algorithmic bytes per launch / mean
+launch time from HIP events on its stream), the CPU oracle timed on a bounded
+sample, and secondary measurements (causal varlen prefill TFLOP/s, batched
+continuous-batching decode, padding mask) unless --no-secondary.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode KV GB/s (% of HBM peak) + µs/step; prefill TFLOP/s (% MFMA peak)"
+MALL_DEFEAT_BYTES = 600 * 2**20
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+def time_replays(fn_list, steps, warmup):
+    """Run fn_list[i % n] for warmup then `steps` iterations; returns
+    (total ms for the timed steps, list of per-launch ms from event pairs)."""
+    torch = _torch()
+    n = len(fn_list)
+    for i in range(warmup):
+        fn_list[i % n]()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(st)
+    for i in range(steps):
+        fn_list[i % n]()
+    t1.record(st)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    # per-launch event pairs (separate pass, same stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(st)
+        fn_list[i % n]()
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return total, per
+
+
+def capture(fn):
+    torch = _torch()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="global"):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key, digest):
+    """Per-launch HBM bytes from the committed rocprofv3 counter summary, or
+    None if absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = dict(p.split("=", 1) for p in line.split() if "=" in p)
+        if parts.get("kernel") == kernel_key and parts.get("src") == digest:
+            try:
+                return float(parts["bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def long_decode(args):
+    torch = _torch()
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    w = I.long_decode()
+    B, Hq, Hkv, D, L = w["B"], w["Hq"], w["Hkv"], w["D"], int(w["kv_lens"][0])
+    plan = V.Plan(B, 1, L, Hq, Hkv, D, False, **args.plan_opts)
+    kv_bytes = 2 * L * Hkv * D * 2
+    ncopy = max(1, -(-MALL_DEFEAT_BYTES // kv_bytes))
+    q = I.normal_bf16((B, Hq, D), 10, "cuda")
+    ks = [I.normal_bf16((L, Hkv, D), 11 + 2 * i, "cuda") for i in range(ncopy)]
+    vs = [I.normal_bf16((L, Hkv, D), 12 + 2 * i, "cuda") for i in range(ncopy)]
+    cu_q = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    cu_kv = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device="cuda")
+    fns = []
+    for i in range(ncopy):
+        k, v = ks[i], vs[i]
+        fns.append(lambda k=k, v=v: plan(q, k, v, cu_q, cu_kv, out=out, lse=lse, B=B))
+    graphs = [capture(f) for f in fns]
+    total, _ = time_replays([g.replay for g in graphs], args.steps, args.warmup)
+    _, per = time_replays(fns, max(50, min(args.steps, 400)), 5)
+    ms = total / args.steps
+    alg_bytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4   # K+V, Q, O, LSE
+    per_launch_ms = sorted(per)[len(per) // 2]
+    mean_launch_ms = sum(per) / len(per)
+    info = plan.info
+    src = ["varlen_gqa_attention_amd/csrc/decode.hip", "varlen_gqa_attention_amd/csrc/device.hpp"]
+    digest = source_digest(src)
+    traffic = stored_traffic("decode_long", digest)
+    res = dict(
+        metric=METRIC, value=round(kv_bytes / (ms * 1e-3) / 1e9, 1), unit="GB/s",
+        ms_per_step=round(ms, 5), us_per_step=round(ms * 1e3, 2),
+        kv_bytes_per_step=kv_bytes, frac_hbm_peak=round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        config=dict(workload="long decode: B=1, Hq=64, Hkv=8, D=128, Lk=32768, bf16 THD, "
+                             f"{ncopy} rotating K/V copies (MALL defeat), graph replay",
+                    B=B, Hq=Hq, Hkv=Hkv, D=D, kv_len=L, nsplit=info["nsplit"],
+                    decode_path=("mfma" if info["decode_path"] == 2 else "wave"),
+                    grid=info["grid"], threads=info["threads"],
+                    fused_combine=info["fused_combine"]),
+        roofline=dict(bound="hbm", achieved=round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1),
+                      peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      traffic=traffic, kernel="decode split + merge (one execute)",
+                      bytes_per_launch=alg_bytes, mean_launch_us=round(mean_launch_ms * 1e3, 2),
+                      median_launch_us=round(per_launch_ms * 1e3, 2), src_digest=digest),
+    )
+    state = dict(plan=plan, q=q, k=ks[0], v=vs[0], cu_q=cu_q, cu_kv=cu_kv, B=B, L=L)
+    return res, state
+
+
+def cpu_baseline_long_decode(state, budget_s):
+    import numpy as np
+    from oracle import attention as A
+    from varlen_gqa_attention_amd import inputs as I
+    q = I.bf16_to_f64(state["q"])
+    k = I.bf16_to_f64(state["k"])
+    v = I.bf16_to_f64(state["v"])
+    L = state["L"]
+    B = state["B"]
+    cu_q, cu_kv = np.array([0, 1]), np.array([0, L])
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        A.attend_varlen(q, k, v, cu_q, cu_kv, B, False)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s or n >= 50:
+            break
+    dt = (time.perf_counter() - t0) / n
+    kv_bytes = 2 * L * k.shape[1] * k.shape[2] * 2
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    cores = min(len(os.sched_getaffinity(0)), max(1, blas))
+    return dict(value=round(kv_bytes / dt / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{n} full long-decode step(s) of the fp64 NumPy oracle "
+                       f"({dt:.2f} s each; K/V of bf16 values copied to host, untimed)")
+
+
+def prefill_measure(args, reps=5):
+    torch = _torch()
+    import numpy as np
+    import varlen_gqa_attention_amd as V
+    from oracle.attention import causal_pairs
+    from varlen_gqa_attention_amd import inputs as I
+    w = I.varlen_prefill(0)
+    m = I.materialise(w, 0, "cuda")
+    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], True)
+    out = torch.empty_like(m["q"])
+    lse = torch.empty(m["q"].shape[:2], device="cuda")
+    pairs = causal_pairs(m["cu_q_np"], m["cu_kv_np"], w["B"], True)
+    flop = 4 * w["Hq"] * w["D"] * pairs
+    f = lambda: plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], out=out, lse=lse, B=w["B"])
+    total, per = time_replays([f], reps, 2)
+    ms = min(per)
+    tq = plan.info["q_tokens_per_tile"]
+    # exact grid: live tiles only, longest first (host knows lengths here)
+    lens = w["q_lens"]
+    tiles = sorted(((b << 16) | t for b, L in enumerate(lens) for t in range(-(-int(L) // tq))),
+                   key=lambda e: -(e & 0xFFFF))
+    tmap = torch.tensor(tiles, dtype=torch.int32, device="cuda")
+    fe = lambda: plan.execute_exact_grid(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], tmap,
+                                         out, lse, w["B"])
+    _, per_e = time_replays([fe], reps, 2)
+
+    def roundtrip():  # the D2H + host cumsum + H2D path the grid-sizing issue describes
+        lens_h = (m["cu_q"][1:w["B"] + 1] - m["cu_q"][:w["B"]]).cpu().numpy()
+        tl = [(b << 16) | t for b, L in enumerate(lens_h) for t in range(-(-int(L) // tq))]
+        tm = torch.tensor(tl, dtype=torch.int32).to("cuda", non_blocking=False)
+        plan.execute_exact_grid(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], tm, out, lse,
+                                w["B"])
+    _, per_r = time_replays([roundtrip], reps, 2)
+    tfl = flop / (ms * 1e-3) / 1e12
+    return dict(workload="causal varlen prefill: B=16, L~U[64,4096] (seed 3,0), Hq=32, Hkv=8, "
+                         "D=128, s_max 4096", flop=flop, causal_pairs=pairs,
+                us=round(ms * 1e3, 1), tflops=round(tfl, 1),
+                frac_mfma_peak=round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                grid=plan.info["grid"], live_tiles=len(tiles) * w["Hkv"],
+                exact_grid_us=round(min(per_e) * 1e3, 1),
+                exact_grid_with_host_roundtrip_us=round(min(per_r) * 1e3, 1))
+
+
+def batched_decode_measure(args, steps=100):
+    torch = _torch()
+    import numpy as np
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    ws = [I.batched_decode_step(t) for t in range(steps)]
+    w = ws[0]
+    B, Hq, Hkv, D, smax = w["B"], w["Hq"], w["Hkv"], w["D"], w["s_max_kv"]
+    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False, **args.plan_opts)
+    pool = B * smax  # room for B sequences of s_max rows: 1 GiB per K/V tensor
+    q = I.normal_bf16((B, Hq, D), 20, "cuda")
+    k = I.normal_bf16((pool, Hkv, D), 21, "cuda")
+    v = I.normal_bf16((pool, Hkv, D), 22, "cuda")
+    # per-step offsets: sequence b starts at b * smax (+ a per-step shift) with length L_b
+    cus = []
+    kv_bytes = []
+    for t, wt in enumerate(ws):
+        # this step's sequences packed back to back from the start of the pool
+        cu = np.concatenate([[0], np.cumsum(wt["kv_lens"])]).astype(np.int32)
+        cus.append(cu)
+        kv_bytes.append(int(wt["kv_lens"].sum()) * Hkv * D * 2 * 2)
+    cu_all = torch.from_numpy(np.stack(cus)).cuda()
+    live = torch.zeros(1, B + 1, dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cu_q = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device="cuda")
+
+    def one():
+        torch.index_select(cu_all, 0, step, out=live)
+        plan(q, k, v, cu_q, live.view(-1), out=out, lse=lse, B=B)
+        step.add_(1)
+    g = capture(one)
+    step.zero_()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    t_host0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    t_host1 = time.perf_counter()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert int(step.item()) == steps
+    mean_bytes = sum(kv_bytes) / steps
+    return dict(workload="continuous-batching decode: B=64, Hq=32, Hkv=8, D=128, s_max_kv=8192, "
+                         "lengths U[128,8192] per step (seed 2,t), 100 graph replays",
+                us_per_step=round(ms * 1e3, 1), kv_gbs=round(mean_bytes / (ms * 1e-3) / 1e9, 1),
+                frac_hbm_peak=round(mean_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                host_enqueue_us_per_step=round((t_host1 - t_host0) / steps * 1e6, 1),
+                decode_path=("mfma" if plan.info["decode_path"] == 2 else "wave"),
+                nsplit=plan.info["nsplit"])
+
+
+def mask_measure():
+    torch = _torch()
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    lens = I.edge_sweep_lengths(64)
+    cu = torch.from_numpy(I.cu_from_lengths(lens, 65, [-1, 2**31 - 1, int(lens.sum())])).cuda()
+    out = torch.empty((33, 1, 1, 16384), dtype=torch.bool, device="cuda")
+    f = lambda: V.padding_mask(cu, 33, 16384, out=out)
+    _, per = time_replays([f], 50, 5)
+    return dict(workload="padding mask B=33, max_seqlen=16384 (540672 bytes)",
+                us=round(sorted(per)[len(per) // 2] * 1e3, 2))
+
+
+def calibrate_copy():
+    """Plain elementwise copy of a known size, for scaling HBM counters."""
+    torch = _torch()
+    n = 256 * 2**20 // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n * 4, "bytes_written": n * 4}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--force-nsplit", type=int, default=0)
+    ap.add_argument("--decode-path", type=int, default=0, choices=[0, 1, 2])
+    ap.add_argument("--fuse-combine", type=int, default=0, choices=[0, 1, 2])
+    ap.add_argument("--workload", default="long_decode",
+                    choices=["long_decode", "prefill", "batched_decode"],
+                    help="headline workload (default: long decode); the others are for "
+                         "profiling runs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    args.plan_opts = dict(force_nsplit=args.force_nsplit, force_decode_path=args.decode_path,
+                          fuse_combine=args.fuse_combine)
+    torch = _torch()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.workload != "long_decode":
+        fn = prefill_measure if args.workload == "prefill" else batched_decode_measure
+        print(json.dumps({"workload": args.workload, **fn(args)}))
+        return
+    res, state = long_decode(args)
+    line = dict(metric=res.pop("metric"), value=res.pop("value"), unit=res.pop("unit"),
+                n_gpus=1, steps=args.steps, warmup=args.warmup,
+                ms_per_step=res.pop("ms_per_step"), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16", data="synthetic")
+    line.update(res)
+    if not args.no_secondary:
+        line["prefill"] = prefill_measure(args)
+        line["batched_decode"] = batched_decode_measure(args)
+        line["padding_mask"] = mask_measure()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
