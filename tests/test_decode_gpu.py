@@ -165,3 +165,33 @@ def test_b_zero_is_noop():
     plan(q, k, k, cu, cu, out=out, lse=lse, B=0)
     torch.cuda.synchronize()
     assert bool((out == 3.0).all()) and bool((lse == 3.0).all())
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("nsplit", [2, 7, 32])
+def test_fused_merge_equals_combine_kernel_bitwise(path, nsplit):
+    """The in-kernel merge (last split workgroup) and the combine kernel use
+    the same arithmetic order: identical bits. Repeated launches of the fused
+    plan must also repeat exactly (its arrival counters reset themselves)."""
+    w = _w("fused vs combine", 5, 16, 2, 128, [0, 1, 700, 2049, 4000], s_max_kv=4096)
+    a = run_decode(w, 31, force_decode_path=path, force_nsplit=nsplit, fuse_combine=2)
+    assert a["info"]["fused_combine"] == 0 and a["info"]["combine_grid"] > 0
+    b = run_decode(w, 31, force_decode_path=path, force_nsplit=nsplit, fuse_combine=1)
+    assert b["info"]["fused_combine"] == 1
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+
+
+def test_fused_plan_repeats_exactly():
+    import varlen_gqa_attention_amd as V
+    w = _w("fused repeat", 3, 64, 8, 128, [5000, 3, 9000], s_max_kv=9000)
+    m = I.materialise(w, 32, "cuda")
+    plan = V.Plan(3, 1, 9000, 64, 8, 128, False, force_nsplit=13)
+    assert plan.info["fused_combine"] == 1
+    outs = []
+    for _ in range(4):
+        o, l = plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], B=3)
+        outs.append((o.clone(), l.clone()))
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])

@@ -16,8 +16,9 @@
 struct vattn_plan_s {
   vattn_plan_info info;
   int device;
-  uint8_t* scratch;  // error word | (m, l) partials | O partials
+  uint8_t* scratch;  // error word | merge counters | (m, l) partials | O partials
   int32_t* err;
+  int32_t* counters;
   float2* part_ml;
   float* part_o;
 };
@@ -83,8 +84,10 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   if (!p) return VATTN_ERR_OOM;
   p->info = info;
   p->device = dev;
-  // layout: [0, 256) error word; then (m, l) pairs; then O partials (256-aligned)
-  uintptr_t off_ml = 256;
+  // layout: [0, 256) error word; merge counters; (m, l) pairs; O partials
+  const uintptr_t n_cnt = info.direct ? 0 : (uintptr_t)info.n_units;
+  const uintptr_t off_cnt = 256;
+  uintptr_t off_ml = align_up(off_cnt + n_cnt * sizeof(int32_t), 256);
   uintptr_t n_part = info.direct ? 0 : (uintptr_t)B_max * Hq * info.nsplit;
   uintptr_t off_o = align_up(off_ml + n_part * sizeof(float2), 256);
   uintptr_t total = off_o + n_part * (uintptr_t)D * sizeof(float);
@@ -98,11 +101,13 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   }
   p->scratch = (uint8_t*)mem;
   p->err = (int32_t*)mem;
+  p->counters = n_cnt ? (int32_t*)(p->scratch + off_cnt) : nullptr;
   p->part_ml = n_part ? (float2*)(p->scratch + off_ml) : nullptr;
   p->part_o = n_part ? (float*)(p->scratch + off_o) : nullptr;
   // plan creation may synchronise (it is not on the hot path): zero the
   // error word once with a kernel, then wait for it.
   if (vattn::launch_clear_word(p->err, nullptr) != hipSuccess ||
+      vattn::launch_clear_words(p->counters, (int)n_cnt, nullptr) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(mem);
     delete p;
@@ -158,10 +163,12 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.part_o = p->part_o;
     a.part_ml = p->part_ml;
     a.err = p->err;
+    a.counters = p->counters;
     a.B = B;
     a.Hq = in.Hq;
     a.Hkv = in.Hkv;
     a.G = in.Hq / in.Hkv;
+    a.D = in.D;
     a.head_blocks = in.head_blocks;
     a.nsplit = in.nsplit;
     a.chunk_keys = in.chunk_keys;
@@ -171,7 +178,8 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.kv_rows = kv_rows;
     a.c = c;
     a.direct = in.direct;
-    e = vattn::launch_decode(a, in.D, in.decode_path, in.threads / 64, in.grid, in.combine_grid,
+    a.fused = in.fused_combine;
+    e = vattn::launch_decode(a, in.decode_path, in.threads / 64, in.grid, in.combine_grid,
                              st);
   } else {
     vattn::PrefillArgs a;

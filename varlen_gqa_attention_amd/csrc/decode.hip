@@ -1,18 +1,24 @@
-// Split-KV decode for varlen GQA on gfx950, plus the log-sum-exp combine.
+// Split-KV decode for varlen GQA on gfx950, plus the log-sum-exp merge.
 //
 // Method (AstrAI commit log for csrc/kernels/gqa_decode_attn.cu, split-KV
 // commit; split-K blog post, The Context: Why Split-K Matters): the KV range
 // of each (sequence, kv head) is cut into `nsplit` contiguous chunks that run
 // on separate workgroups; each emits an unnormalised partial (O, m, l) and a
-// combine kernel merges them by log-sum-exp. With one split the same
-// workgroup normalises and writes the output directly.
+// log-sum-exp merge combines them. With one split the same workgroup
+// normalises and writes the output directly. The merge runs either in a
+// separate combine kernel or, by default, inside the split kernel: the last
+// split workgroup of a unit to finish (a device-scope counter, reset by that
+// workgroup so the next launch or graph replay starts from zero) merges the
+// unit's partials, which saves a launch and the combine kernel's round trips.
 //
 // Workgroup = (sequence b, kv head hk, head block hb, split s). Its waves take
 // the 32-key tiles of the chunk round-robin, keep their own running
 // (m, l, O) state, and merge through LDS at the end, so the tile loop itself
-// has no workgroup barrier. Softmax works in base 2 on t = s * scale * log2(e)
-// (the scale folds into the exponent's FMA in fp32; Q is not rounded after
-// scaling); outputs convert back with ln 2.
+// has no workgroup barrier. Each wave double-buffers its tiles in registers
+// (two tiles in flight, ping-pong without register copies, so the wait for a
+// tile never covers the tile issued after it). Softmax works in base 2 on
+// t = s * scale * log2(e) (the scale folds into the exponent in fp32; Q is not
+// rounded after scaling); outputs convert back with ln 2.
 //
 // Two compute paths (dispatch between an MMA and a scalar kernel by G, as in
 // the AstrAI "dispatch_decode" commit):
@@ -51,7 +57,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 struct UnitCoords {
-  int b, hk, hb, s;
+  int b, hk, hb, s, unit;
 };
 
 __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
@@ -59,6 +65,7 @@ __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
   UnitCoords u;
   u.s = bid % a.nsplit;
   bid /= a.nsplit;
+  u.unit = bid;
   u.hb = bid % a.head_blocks;
   bid /= a.head_blocks;
   u.hk = bid % a.Hkv;
@@ -66,13 +73,88 @@ __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
   return u;
 }
 
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int qrow, int hq, int d, float val) {
+  __bf16 ob = (__bf16)val;
+  a.out[((int64_t)qrow * a.Hq + hq) * a.D + d] = __builtin_bit_cast(uint16_t, ob);
+}
+
+// Writes O = 0, LSE = -inf (no visible key) for heads [h0, h0 + nh).
+__device__ __forceinline__ void store_empty(const DecodeArgs& a, int qrow, int h0, int nh) {
+  for (int idx = threadIdx.x; idx < nh * a.D; idx += blockDim.x) {
+    const int h = idx / a.D, d = idx % a.D;
+    store_out(a, qrow, h0 + h, d, 0.f);
+    if (d == 0) a.lse[(int64_t)qrow * a.Hq + h0 + h] = kNegInf;
+  }
+}
+
+// Partial loads. In the fused merge the partials of other workgroups (other
+// XCDs, other L2s) are read with system-scope loads, which bypass the caches;
+// they were written with system-scope (write-through) stores.
+template <bool COHERENT>
+__device__ __forceinline__ float ld_part(const float* p) {
+  if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  else return *p;
+}
+template <bool COHERENT>
+__device__ __forceinline__ void st_part(float* p, float v) {
+  if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  else *p = v;
+}
+
+// LSE merge of the first n_live split partials of heads [h0, h0 + nh) of
+// sequence b, written as bf16 out and fp32 LSE. Used by the combine kernel
+// and by the fused merge, with the same arithmetic order in both. All of a
+// thread's partial loads are issued before the first is used.
+template <int D, bool COHERENT>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int qrow, int h0, int nh,
+                                               int n_live) {
+  const float* pml = reinterpret_cast<const float*>(a.part_ml);
+  constexpr int CH = 32;
+  for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
+    const int h = idx / D, d = idx % D;
+    const int hq = h0 + h;
+    const int64_t base = (int64_t)(b * a.Hq + hq) * a.nsplit;
+    // loads are unconditional (indices clamped to the last live split) so a
+    // chunk's loads are all in flight at once; extra slots get weight 0
+    float M = kNegInf;
+    for (int s0 = 0; s0 < n_live; s0 += CH) {
+      float mv[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) mv[j] = ld_part<COHERENT>(pml + 2 * (base + min(s0 + j, n_live - 1)));
+#pragma unroll
+      for (int j = 0; j < CH; ++j) M = fmaxf(M, mv[j]);
+    }
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < n_live; s0 += CH) {
+      float mm[CH], ll[CH], po[CH];
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int64_t sj = base + min(s0 + j, n_live - 1);
+        mm[j] = ld_part<COHERENT>(pml + 2 * sj);
+        ll[j] = ld_part<COHERENT>(pml + 2 * sj + 1);
+        po[j] = ld_part<COHERENT>(a.part_o + sj * D + d);
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const float wt = (s0 + j < n_live) ? fast_exp2(mm[j] - Ms) : 0.f;
+        L += wt * ll[j];
+        O += wt * po[j];
+      }
+    }
+    store_out(a, qrow, hq, d, (L > 0.f) ? O / L : 0.f);
+    if (d == 0) a.lse[(int64_t)qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  }
+}
+
 // Cross-wave merge of per-wave (m, l, O) states held in LDS, then the
-// epilogue: direct (normalised bf16 out + LSE) or split partial.
+// epilogue: direct (normalised bf16 out + LSE) or split partial; in fused
+// mode the last split workgroup of the unit then merges all partials.
 // mo: [NW][HPB][D] floats, mm / ml: [NW][HPB].
 template <int D, int NW, int HPB>
-__device__ __forceinline__ void merge_and_store(const DecodeArgs& a, const UnitCoords& u,
-                                                int qrow, int h0, int nh, const float* mo,
-                                                const float* mm, const float* ml) {
+__device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const UnitCoords& u, int Lk,
+                                                 int qrow, int h0, int nh, const float* mo,
+                                                 const float* mm, const float* ml, int* flag) {
   for (int idx = threadIdx.x; idx < nh * D; idx += NW * 64) {
     const int h = idx / D, d = idx % D;
     float M = kNegInf;
@@ -88,17 +170,46 @@ __device__ __forceinline__ void merge_and_store(const DecodeArgs& a, const UnitC
     }
     const int hq = h0 + h;
     if (a.direct) {
-      const float val = (L > 0.f) ? O / L : 0.f;
-      __bf16 ob = (__bf16)val;
-      a.out[((int64_t)qrow * a.Hq + hq) * D + d] = __builtin_bit_cast(uint16_t, ob);
+      store_out(a, qrow, hq, d, (L > 0.f) ? O / L : 0.f);
       if (d == 0)
         a.lse[(int64_t)qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
     } else {
       const int64_t pidx = ((int64_t)(u.b * a.Hq + hq) * a.nsplit + u.s);
-      a.part_o[pidx * D + d] = O;
-      if (d == 0) a.part_ml[pidx] = make_float2(M, L);
+      float* pml = reinterpret_cast<float*>(a.part_ml);
+      if (a.fused) {
+        st_part<true>(a.part_o + pidx * D + d, O);
+        if (d == 0) {
+          st_part<true>(pml + 2 * pidx, M);
+          st_part<true>(pml + 2 * pidx + 1, L);
+        }
+      } else {
+        st_part<false>(a.part_o + pidx * D + d, O);
+        if (d == 0) {
+          st_part<false>(pml + 2 * pidx, M);
+          st_part<false>(pml + 2 * pidx + 1, L);
+        }
+      }
     }
   }
+  if (a.direct || !a.fused) return;
+  // Fused merge. The partials above were written through to memory; once
+  // every thread's stores have completed (the wait below) the workgroup counts
+  // itself in with a system-scope atomic, and the last live split of the unit
+  // reads all partials with cache-bypassing loads and merges them. No L2
+  // write-back or invalidation is needed, unlike a device-scope fence.
+  const int n_live = (Lk + a.chunk_keys - 1) / a.chunk_keys;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev =
+        __hip_atomic_fetch_add(&a.counters[u.unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const int last = (prev == n_live - 1);
+    if (last) __hip_atomic_store(&a.counters[u.unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  merge_partials<D, true>(a, u.b, qrow, h0, nh, n_live);
 }
 
 // ---------------------------------------------------------------------------
@@ -116,6 +227,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int MERGE_BYTES = NW * HPB * D * 4 + 2 * NW * HPB * 4;
   constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ int s_flag;
 
   const UnitCoords u = unit_of_block(a);
   if (u.b >= a.B) return;
@@ -124,12 +236,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   if (u.s == 0 && u.hb == 0 && u.hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
   if (sq.len == 0) return;
   const int Lk = sk.len;
-  const int kbeg = u.s * a.chunk_keys;
-  if (!a.direct && kbeg >= Lk) return;  // empty split: the combine never reads it
-  const int kend = min(kbeg + a.chunk_keys, Lk);
   const int qrow = sq.start;
   const int h0 = u.hk * a.G + u.hb * HPB;
   const int nh = min(HPB, a.G - u.hb * HPB);
+  const int kbeg = u.s * a.chunk_keys;
+  if (!a.direct && kbeg >= Lk) {  // empty split: never merged
+    if (Lk == 0 && u.s == 0 && a.fused) store_empty(a, qrow, h0, nh);
+    return;
+  }
+  const int kend = min(kbeg + a.chunk_keys, Lk);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int hl = lane & 15, g4 = lane >> 4;
@@ -170,9 +285,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  u32x4 kr[2][KS], vr[DV];
-  if (w < ntiles) load_tile(w, kr, vr);
-  for (int t = w; t < ntiles; t += NW) {
+  auto process_tile = [&](int t, const u32x4 (&kr)[2][KS], const u32x4 (&vr)[DV]) {
     const int key0 = kbeg + t * TILE;
     // stage V (row-major [key][d], swizzled) in this wave's LDS slice
 #pragma unroll
@@ -191,11 +304,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         sacc[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, kr[kb2][ks]), qv[ks], sacc[kb2], 0, 0, 0);
     }
-    // prefetch the wave's next tile while this one is consumed
-    u32x4 kn[2][KS], vn[DV];
-    const bool more = t + NW < ntiles;
-    if (more) load_tile(t + NW, kn, vn);
-
     // online softmax; lane holds keys 16 kb2 + 4 g4 + i of head hl
     float sc[8];
     float mx = kNegInf;
@@ -245,13 +353,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pt, o[db], 0, 0, 0);
     }
     wave_lds_sync();
-    if (more) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = kn[kb2][ks];
-#pragma unroll
-      for (int i = 0; i < DV; ++i) vr[i] = vn[i];
+  };
+
+  // Two tiles in flight per wave: A holds tile t, B tile t + NW. Loads are
+  // issued unconditionally (past the wave's last tile they re-read that tile,
+  // which the caches still hold) so the number of loads outstanding at every
+  // wait is the same on all paths and each wait covers only the tile it needs.
+  if (w < ntiles) {
+    const int tl = w + NW * ((ntiles - 1 - w) / NW);  // this wave's last tile
+    u32x4 kA[2][KS], vA[DV], kB[2][KS], vB[DV];
+    load_tile(w, kA, vA);
+    load_tile(min(w + NW, tl), kB, vB);
+    for (int t = w; t < ntiles; t += 2 * NW) {
+      process_tile(t, kA, vA);
+      load_tile(min(t + 2 * NW, tl), kA, vA);
+      if (t + NW < ntiles) process_tile(t + NW, kB, vB);
+      load_tile(min(t + 3 * NW, tl), kB, vB);
     }
   }
   // l: each lane summed its own 8 keys per tile; add the four key groups
@@ -270,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     ml[w * HPB + hl] = l;
   }
   __syncthreads();
-  merge_and_store<D, NW, HPB>(a, u, qrow, h0, nh, mo, mm, ml);
+  finish_workgroup<D, NW, HPB>(a, u, Lk, qrow, h0, nh, mo, mm, ml, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -280,10 +397,11 @@ template <int D, int NW, int GM>
 __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;             // lanes per key row (8 d-values each)
   constexpr int RPI = 64 / LPR;          // key rows per load instruction
-  constexpr int TILE = (D <= 128) ? 32 : 16;
+  constexpr int TILE = (D <= 64) ? 32 : 16;  // keys per wave iteration (two tiles in flight)
   constexpr int NI = TILE / RPI;         // loads per tile for K and for V
   constexpr int MERGE_FLOATS = NW * GM * D + 2 * NW * GM;
   __shared__ __attribute__((aligned(16))) float lds[MERGE_FLOATS];
+  __shared__ int s_flag;
 
   const UnitCoords u = unit_of_block(a);
   if (u.b >= a.B) return;
@@ -292,12 +410,15 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   if (u.s == 0 && u.hb == 0 && u.hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
   if (sq.len == 0) return;
   const int Lk = sk.len;
-  const int kbeg = u.s * a.chunk_keys;
-  if (!a.direct && kbeg >= Lk) return;
-  const int kend = min(kbeg + a.chunk_keys, Lk);
   const int qrow = sq.start;
   const int h0 = u.hk * a.G + u.hb * GM;
   const int nh = min(GM, a.G - u.hb * GM);
+  const int kbeg = u.s * a.chunk_keys;
+  if (!a.direct && kbeg >= Lk) {
+    if (Lk == 0 && u.s == 0 && a.fused) store_empty(a, qrow, h0, nh);
+    return;
+  }
+  const int kend = min(kbeg + a.chunk_keys, Lk);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane / LPR, c = lane % LPR;
@@ -331,14 +452,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
     }
   };
 
-  u32x4 kr[NI], vr[NI];
-  if (w < ntiles) load_tile(w, kr, vr);
-  for (int t = w; t < ntiles; t += NW) {
+  auto process_tile = [&](int t, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
     const int key0 = kbeg + t * TILE;
-    u32x4 kn[NI], vn[NI];
-    const bool more = t + NW < ntiles;
-    if (more) load_tile(t + NW, kn, vn);
-
     float s[NI][GM];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -393,12 +508,18 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[g][j] = fmaf(s[i][g], vf[j], o[g][j]);
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kr[i] = kn[i];
-        vr[i] = vn[i];
-      }
+  };
+
+  if (w < ntiles) {  // two tiles in flight, unconditional loads (see the MFMA path)
+    const int tl = w + NW * ((ntiles - 1 - w) / NW);
+    u32x4 kA[NI], vA[NI], kB[NI], vB[NI];
+    load_tile(w, kA, vA);
+    load_tile(min(w + NW, tl), kB, vB);
+    for (int t = w; t < ntiles; t += 2 * NW) {
+      process_tile(t, kA, vA);
+      load_tile(min(t + 2 * NW, tl), kA, vA);
+      if (t + NW < ntiles) process_tile(t + NW, kB, vB);
+      load_tile(min(t + 3 * NW, tl), kB, vB);
     }
   }
   // add the row groups' partial sums (their m are identical)
@@ -428,11 +549,11 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  merge_and_store<D, NW, GM>(a, u, qrow, h0, nh, mo, mm, ml);
+  finish_workgroup<D, NW, GM>(a, u, Lk, qrow, h0, nh, mo, mm, ml, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
-// LSE combine: one workgroup per (sequence, query head)
+// LSE combine kernel: one workgroup per (sequence, query head)
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
@@ -442,23 +563,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (sq.len == 0) return;
   const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
   const int n_live = (sk.len + a.chunk_keys - 1) / a.chunk_keys;
-  const int64_t base = (int64_t)(b * a.Hq + h) * a.nsplit;
-  float M = kNegInf;
-  for (int s = 0; s < n_live; ++s) M = fmaxf(M, a.part_ml[base + s].x);
-  const float Ms = (M == kNegInf) ? 0.f : M;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < n_live; ++s) {
-      const float2 ml = a.part_ml[base + s];
-      const float wt = fast_exp2(ml.x - Ms);
-      L += wt * ml.y;
-      O += wt * a.part_o[(base + s) * D + d];
-    }
-    const float val = (L > 0.f) ? O / L : 0.f;
-    __bf16 ob = (__bf16)val;
-    a.out[((int64_t)sq.start * a.Hq + h) * D + d] = __builtin_bit_cast(uint16_t, ob);
-    if (d == 0) a.lse[(int64_t)sq.start * a.Hq + h] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
-  }
+  merge_partials<D, false>(a, b, sq.start, h, 1, n_live);
+}
+
+__global__ void clear_words_kernel(int32_t* w, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) w[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -475,20 +584,27 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int gri
     else decode_wave_kernel<D, 4, 4><<<grid, 256, 0, st>>>(a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.direct) return e;
+  if (e != hipSuccess || a.direct || a.fused) return e;
   decode_combine_kernel<D><<<combine_grid, D < 64 ? 64 : D, 0, st>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int D, int path, int nw, int grid, int combine_grid,
+hipError_t launch_decode(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
                          hipStream_t st) {
-  switch (D) {
+  switch (a.D) {
     case 32: return launch_decode_d<32>(a, path, nw, grid, combine_grid, st);
     case 64: return launch_decode_d<64>(a, path, nw, grid, combine_grid, st);
     case 128: return launch_decode_d<128>(a, path, nw, grid, combine_grid, st);
     case 256: return launch_decode_d<256>(a, path, nw, grid, combine_grid, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_clear_words(int32_t* w, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  clear_words_kernel<<<blocks, 256, 0, st>>>(w, n);
+  return hipGetLastError();
 }
 
 }  // namespace vattn

@@ -16,13 +16,15 @@ struct DecodeArgs {
   float* part_o;    // [B_max, Hq, nsplit, D] unnormalised partial outputs
   float2* part_ml;  // [B_max, Hq, nsplit] (m in log2 units, l)
   int32_t* err;
-  int B, Hq, Hkv, G;
+  int32_t* counters;  // [n_units] arrival counters of the fused merge (kept at 0 between launches)
+  int B, Hq, Hkv, G, D;
   int head_blocks;  // workgroups per (b, hk) along the head dimension
   int nsplit, chunk_keys;
   int s_max_q, s_max_kv;
   int64_t q_rows, kv_rows;
   float c;          // softmax scale * log2(e)
   int direct;       // 1: normalise and write out/lse; 0: write partials
+  int fused;        // with direct == 0: 1 = last split workgroup merges, 0 = combine kernel
 };
 
 struct PrefillArgs {
@@ -45,8 +47,9 @@ struct PrefillArgs {
   int causal;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, int D, int path, int nw, int grid, int combine_grid,
+hipError_t launch_decode(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
                          hipStream_t st);
+hipError_t launch_clear_words(int32_t* words, int n, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st);
 hipError_t launch_padding_mask(const int32_t* cu, int B, int max_seqlen, uint8_t* mask,
                                hipStream_t st);

@@ -84,11 +84,13 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     // in flight.
     // (D = 256 stays at 4 waves: 8 would exceed the register file.)
     in.threads = (in.grid <= n_cu && D <= 128) ? 512 : 256;
-    in.fused_combine = 0;
-    in.combine_grid = in.direct ? 0 : B_max * Hq;
+    // the merge runs in the split kernel unless disabled (then: combine kernel)
+    in.fused_combine = (!in.direct && o.fuse_combine != 2) ? 1 : 0;
+    in.combine_grid = (in.direct || in.fused_combine) ? 0 : B_max * Hq;
     in.scratch_bytes = 256;  // error word, aligned
     if (!in.direct)
-      in.scratch_bytes += (int64_t)B_max * Hq * nsplit * ((int64_t)D * 4 + 8);
+      in.scratch_bytes += (int64_t)in.n_units * 4 + 256 +
+                          (int64_t)B_max * Hq * nsplit * ((int64_t)D * 4 + 8) + 256;
   } else {
     if (G > kPrefillRows) return VATTN_ERR_UNSUPPORTED;
     in.q_tokens_per_tile = kPrefillRows / G;
