@@ -332,6 +332,8 @@ def main():
     ap.add_argument("--force-nsplit", type=int, default=0)
     ap.add_argument("--decode-path", type=int, default=0, choices=[0, 1, 2])
     ap.add_argument("--fuse-combine", type=int, default=0, choices=[0, 1, 2])
+    ap.add_argument("--nsplit-cap", type=int, default=0)
+    ap.add_argument("--decode-waves", type=int, default=0, choices=[0, 4, 8])
     ap.add_argument("--workload", default="long_decode",
                     choices=["long_decode", "prefill", "batched_decode"],
                     help="headline workload (default: long decode); the others are for "
@@ -342,7 +344,8 @@ def main():
                                    "(multi-GPU sharding is described in DESIGN.md, not built)"}))
         sys.exit(2)
     args.plan_opts = dict(force_nsplit=args.force_nsplit, force_decode_path=args.decode_path,
-                          fuse_combine=args.fuse_combine)
+                          fuse_combine=args.fuse_combine, nsplit_cap=args.nsplit_cap,
+                          decode_waves=args.decode_waves)
     torch = _torch()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)

@@ -94,7 +94,8 @@ typedef struct {
   int force_nsplit;         /* > 0: use this split count (capped by the tile count) */
   int force_decode_path;    /* VATTN_DECODE_* */
   int n_cu_override;        /* > 0: plan as if the device had this many CUs */
-  int fuse_combine;         /* 1: last split workgroup of a unit merges (no 2nd launch); 2: force off */
+  int fuse_combine;         /* 1: last split workgroup of a unit merges (no 2nd launch); 0/2: combine kernel */
+  int decode_waves;         /* 4 or 8 waves per decode workgroup; 0 = automatic */
 } vattn_plan_opts;
 
 typedef struct {

@@ -185,7 +185,7 @@ def test_fused_plan_repeats_exactly():
     import varlen_gqa_attention_amd as V
     w = _w("fused repeat", 3, 64, 8, 128, [5000, 3, 9000], s_max_kv=9000)
     m = I.materialise(w, 32, "cuda")
-    plan = V.Plan(3, 1, 9000, 64, 8, 128, False, force_nsplit=13)
+    plan = V.Plan(3, 1, 9000, 64, 8, 128, False, force_nsplit=13, fuse_combine=1)
     assert plan.info["fused_combine"] == 1
     outs = []
     for _ in range(4):

@@ -12,8 +12,8 @@ from varlen_gqa_attention_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("nsplit", [0, 4])
-def test_graph_replay_with_changing_lengths(nsplit):
+@pytest.mark.parametrize("nsplit,fuse", [(0, 0), (4, 0), (4, 1)])
+def test_graph_replay_with_changing_lengths(nsplit, fuse):
     import varlen_gqa_attention_amd as V
     B, Hq, Hkv, D, smax, steps = 16, 32, 8, 128, 2048, 12
     lens = [I.uniform_lengths(B, 1, smax, 2, t) for t in range(steps)]
@@ -29,7 +29,7 @@ def test_graph_replay_with_changing_lengths(nsplit):
     lse = torch.zeros(B, Hq, device="cuda")
     outs = torch.zeros(steps, B, Hq, D, dtype=torch.bfloat16, device="cuda")
     lses = torch.zeros(steps, B, Hq, device="cuda")
-    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False, force_nsplit=nsplit)
+    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False, force_nsplit=nsplit, fuse_combine=fuse)
     print(f"[graph] plan {plan.info}", flush=True)
 
     def one_step():

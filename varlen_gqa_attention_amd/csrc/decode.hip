@@ -60,11 +60,16 @@ struct UnitCoords {
   int b, hk, hb, s, unit;
 };
 
+// Workgroup i = split (i / n_units) of unit (i % n_units): consecutive
+// workgroups are different units at the same split, so with workgroups
+// dispatched round-robin over the 8 XCDs each XCD streams whole units (for
+// 8 units, one KV head per XCD) rather than a slice of every head.
 __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
   int bid = blockIdx.x;
   UnitCoords u;
-  u.s = bid % a.nsplit;
-  bid /= a.nsplit;
+  const int n_units = gridDim.x / a.nsplit;
+  u.s = bid / n_units;
+  bid = bid % n_units;
   u.unit = bid;
   u.hb = bid % a.head_blocks;
   bid /= a.head_blocks;

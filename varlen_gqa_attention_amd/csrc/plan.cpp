@@ -84,8 +84,11 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     // in flight.
     // (D = 256 stays at 4 waves: 8 would exceed the register file.)
     in.threads = (in.grid <= n_cu && D <= 128) ? 512 : 256;
-    // the merge runs in the split kernel unless disabled (then: combine kernel)
-    in.fused_combine = (!in.direct && o.fuse_combine != 2) ? 1 : 0;
+    if (o.decode_waves == 4 || (o.decode_waves == 8 && D <= 128)) in.threads = 64 * o.decode_waves;
+    // the merge runs in a separate combine kernel unless the in-kernel merge
+    // is asked for (on this chip the two cost about the same: the in-kernel
+    // merge saves a launch but serialises write-through, atomic and reads)
+    in.fused_combine = (!in.direct && o.fuse_combine == 1) ? 1 : 0;
     in.combine_grid = (in.direct || in.fused_combine) ? 0 : B_max * Hq;
     in.scratch_bytes = 256;  // error word, aligned
     if (!in.direct)

@@ -22,12 +22,12 @@ int main() {
   // one long sequence, 8 KV heads, 256 CUs: the cap of 32 binds
   CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.is_decode && in.nsplit == 32 && in.grid == 256 && in.chunk_keys == 1024 && !in.direct);
-  CHECK(in.decode_path == VATTN_DECODE_MFMA && in.fused_combine == 1 && in.combine_grid == 0);
+  CHECK(in.decode_path == VATTN_DECODE_MFMA && in.fused_combine == 0 && in.combine_grid == 64);
   {
-    vattn_plan_opts sep = {};
-    sep.fuse_combine = 2;  // separate combine kernel: one workgroup per (sequence, query head)
-    CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, &sep, 256, &in) == VATTN_OK);
-    CHECK(in.fused_combine == 0 && in.combine_grid == 64 && in.nsplit == 32);
+    vattn_plan_opts fu = {};
+    fu.fuse_combine = 1;  // in-kernel merge: no combine launch
+    CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, &fu, 256, &in) == VATTN_OK);
+    CHECK(in.fused_combine == 1 && in.combine_grid == 0 && in.nsplit == 32);
   }
   // batch * kv heads fills the device: direct write
   CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
