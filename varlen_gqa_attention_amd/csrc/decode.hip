@@ -38,7 +38,7 @@
 namespace vattn {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef bf16x2 bf16x2_t;
 
 // Reinterpret one 32-bit word as two bf16. The word is taken by value: this
 // hipcc miscompiles __builtin_bit_cast applied directly to an ext-vector

@@ -25,11 +25,12 @@ constexpr int kErrRows = 0x4;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round two floats to bf16 (nearest-even) and pack them, low half first.
+// Round two floats to bf16 (nearest-even) and pack them, low half first
+// (one v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  uint16_t ua = __builtin_bit_cast(uint16_t, a), ub = __builtin_bit_cast(uint16_t, b);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

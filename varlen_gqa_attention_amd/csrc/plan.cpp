@@ -95,8 +95,8 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
       in.scratch_bytes += (int64_t)in.n_units * 4 + 256 +
                           (int64_t)B_max * Hq * nsplit * ((int64_t)D * 4 + 8) + 256;
   } else {
-    if (G > kPrefillRows) return VATTN_ERR_UNSUPPORTED;
-    in.q_tokens_per_tile = kPrefillRows / G;
+    if (G > prefill_rows(D)) return VATTN_ERR_UNSUPPORTED;
+    in.q_tokens_per_tile = prefill_rows(D) / G;
     in.n_qtiles = cdiv(s_max_q, in.q_tokens_per_tile);
     if (in.n_qtiles > 65535) return VATTN_ERR_UNSUPPORTED;
     const int64_t units = (int64_t)B_max * Hkv;
@@ -104,7 +104,7 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     if (grid > (1LL << 31) - 1) return VATTN_ERR_UNSUPPORTED;
     in.n_units = (int)units;
     in.grid = (int)grid;
-    in.threads = 256;
+    in.threads = prefill_threads(D);
     in.block_n = 64;
     in.n_tiles = cdiv(s_max_kv, 64);
     in.nsplit = 1;

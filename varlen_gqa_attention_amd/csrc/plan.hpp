@@ -10,7 +10,10 @@ constexpr int kDecodeBlockN = 64;     // decode KV tile used by the split rule (
 constexpr int kDecodeMfmaHeads = 16;  // heads per workgroup on the MFMA decode path
 constexpr int kDecodeWaveHeads = 4;   // heads per workgroup on the wave decode path
 constexpr int kWaveMaxG = 4;          // auto: G <= this uses the wave path
-constexpr int kPrefillRows = 128;     // query rows (heads x tokens) per prefill workgroup
+// query rows (heads x tokens) per prefill workgroup: 8 waves (4 for D = 256)
+// of 32 rows; threads per prefill workgroup
+constexpr int prefill_rows(int D) { return D <= 128 ? 256 : 128; }
+constexpr int prefill_threads(int D) { return D <= 128 ? 512 : 256; }
 
 // Fills *info (sizes only; no allocation). n_cu must be > 0.
 vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv, int D,

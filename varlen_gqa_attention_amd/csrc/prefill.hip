@@ -1,27 +1,35 @@
 // Causal varlen prefill for GQA on gfx950 (online softmax, bf16 MFMA).
 //
 // A workgroup owns one query tile of one sequence for one KV head: the G query
-// heads of that KV head are folded into the 128 rows of the tile (rows =
-// heads x tq tokens, tq = 128 / G; kernbench ADR commit page, "GQA via M-fold"
-// finding), so every K/V tile brought into LDS serves all G heads. Its 4 waves
-// own 32 rows each. The grid is sized at plan time from B_max and s_max_q;
-// each workgroup reads its sequence's offsets from cu_seqlens on the device
-// and exits at once when its tile lies past the real length (cudnn-frontend
-// issue #552, How the other backends avoid this: tiles read device lengths
-// and early-exit).
+// heads of that KV head are folded into the rows of the tile (rows = heads x
+// tq tokens; kernbench ADR commit page, "GQA via M-fold" finding), so every
+// K/V tile brought into LDS serves all G heads. The grid is sized at plan time
+// from B_max and s_max_q; each workgroup reads its sequence's offsets from
+// cu_seqlens on the device and exits at once when its tile lies past the real
+// length (cudnn-frontend issue #552, How the other backends avoid this: tiles
+// read device lengths and early-exit).
 //
-// Per 64-key tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from a
-// swizzled LDS tile as the A operand, Q^T held in registers as B), online
-// softmax in base 2 with per-lane row state (a lane's scores all belong to
-// one query row), then O^T += V^T P^T where P^T is the S^T accumulator
-// rounded to bf16 in place and V^T comes from the transposed LDS read. Only
-// tiles that cross the causal diagonal or the end of the keys are masked.
+// Layout of the work: 8 waves (4 at D = 256), each owning one block of 32
+// rows. Per 64-key tile, S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from
+// LDS as the A operand; Q^T held in registers), online softmax in base 2 with
+// per-lane row state (all of a lane's scores belong to one query row), then
+// O^T += V^T P^T where P^T is the S^T accumulator rounded to bf16 in place and
+// V^T comes from the gfx950 transposed LDS read. K/V tiles reach a two-stage
+// LDS ring through registers: the global loads of tile jt + 2 are in flight
+// while tile jt is computed, and land in LDS (swizzled, conflict-free) at the
+// start of the next iteration; one workgroup barrier per tile. LDS fragment
+// reads run a few k-steps ahead of the MFMAs that consume them. The softmax
+// scale folds into the exponent's FMA; the running max used for the exponent
+// is only raised when a row's max grows by more than 2^8, so the O accumulator
+// is rescaled rarely (exact: l uses the same reference).
+// Only tiles that cross the causal diagonal or the end of the keys are masked.
 //
 // Workgroup order is XCD-aware: workgroup i runs on XCD i % 8, so the grid is
 // arranged such that each XCD walks whole (sequence, KV head) units, largest
 // query tiles first, keeping a unit's K/V in that XCD's L2 while its tiles run.
 #include "device.hpp"
 #include "launch.hpp"
+#include "plan.hpp"
 
 namespace vattn {
 
@@ -31,24 +39,33 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+// s_waitcnt vmcnt(0) with the other counters untouched (gfx9 encoding).
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+}
+
 template <int D>
 struct PrefillCfg {
-  static constexpr int BN = 64;        // keys per tile
-  static constexpr int CPR = D / 8;    // 16-byte chunks per row
-  static constexpr int KS = D / 16;    // k-steps of 16 for Q K^T
-  static constexpr int DBLK = D / 32;  // 32-wide d blocks of P V
-  static constexpr int LPT = BN * CPR / 256;  // 16-byte loads per thread per tile (K or V)
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int OCC = D <= 128 ? 2 : 1;
+  // 8 waves (two per SIMD) of one 32-row block each for D <= 128; at D = 256
+  // a wave's registers need a SIMD to itself: 4 waves.
+  static constexpr int NW = D <= 128 ? 8 : 4;
+  static constexpr int RB = 1;                   // 32-row blocks per wave
+  static constexpr int ROWS = NW * RB * 32;      // rows per workgroup
+  static constexpr int BN = 64;                  // keys per tile
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int KS = D / 16;              // k-steps of 16 for Q K^T
+  static constexpr int DBLK = D / 32;            // 32-wide d blocks of P V
+  static constexpr int TILE_BYTES = BN * D * 2;  // one K (or V) tile
+  static constexpr int NSTAGE = 2;               // LDS ring depth (K + V per stage)
+  static constexpr int THREADS = NW * 64;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, PrefillCfg<D>::OCC) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D>;
-  constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, LPT = C::LPT;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::TILE_BYTES];
-  uint8_t* lk = lds;
-  uint8_t* lv = lds + C::TILE_BYTES;
+  constexpr int NW = C::NW, RB = C::RB, BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK;
+  constexpr int NSTAGE = C::NSTAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * 2 * C::TILE_BYTES];
 
   // ---- which (sequence, kv head, query tile)
   int b, hk, qt;
@@ -77,163 +94,271 @@ __global__ __launch_bounds__(256, PrefillCfg<D>::OCC) void prefill_kernel(Prefil
   if (t0 >= Lq) return;  // dead tile
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = 32 * w + (lane & 31);
-  const int hl = row / a.tq;
-  const int tok = t0 + row % a.tq;
-  const bool row_ok = hl < a.G && tok < Lq;
-  const int hq = hk * a.G + hl;
   const int shift = Lk - Lq;  // bottom-right causal alignment
-  const int row_lim = a.causal ? tok + shift : Lk - 1;  // last visible key of this row
   const int t_last = min(t0 + a.tq - 1, Lq - 1);
   const int kend = a.causal ? max(0, min(Lk, t_last + shift + 1)) : Lk;
   const int kfull = a.causal ? max(0, min(Lk, t0 + shift + 1)) : Lk;  // keys seen by all rows
 
-  // ---- Q^T operand: lane holds Q[row][16 ks + 8 (lane >> 5) .. +8]
-  bf16x8 qv[KS];
-  {
-    const uint16_t* qp = a.q + ((int64_t)(sq.start + tok) * a.Hq + hq) * D + 8 * (lane >> 5);
+  // ---- per row block: this lane's query row
+  int tok[RB], hq[RB], row_lim[RB];
+  bool row_ok[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = 32 * (RB * w + rb) + (lane & 31);
+    const int hl = row / a.tq;
+    tok[rb] = t0 + row % a.tq;
+    row_ok[rb] = hl < a.G && tok[rb] < Lq;
+    hq[rb] = hk * a.G + hl;
+    row_lim[rb] = a.causal ? tok[rb] + shift : Lk - 1;
+  }
+
+  // ---- Q^T operands: lane holds Q[row][16 ks + 8 (lane >> 5) .. +8]
+  bf16x8 qv[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const uint16_t* qp =
+        a.q + ((int64_t)(sq.start + tok[rb]) * a.Hq + hq[rb]) * D + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = {0, 0, 0, 0};
-      if (row_ok) x = ld16(qp + 16 * ks);
-      qv[ks] = __builtin_bit_cast(bf16x8, x);
+      if (row_ok[rb]) x = ld16(qp + 16 * ks);
+      qv[rb][ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  float m = kNegInf, l = 0.f;
-  f32x16 o[DBLK];
+  // Q must be in registers before the loop: an explicit wait here tells the
+  // compiler's counter tracking so, and the loop's MFMAs then never wait on
+  // the tile prefetches issued inside the loop.
+  wait_vmem_all();
+
+  float m[RB], l[RB];
+  f32x16 o[RB][DBLK];
 #pragma unroll
-  for (int i = 0; i < DBLK; ++i)
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[i][j] = 0.f;
+    for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[rb][i][j] = 0.f;
+  }
 
   const int64_t kvstride = (int64_t)a.Hkv * D;
   const uint16_t* kbase = a.k + ((int64_t)sk.start * a.Hkv + hk) * D;
   const uint16_t* vbase = a.v + ((int64_t)sk.start * a.Hkv + hk) * D;
   const int ntiles = (kend + BN - 1) / BN;
 
-  auto load_tile = [&](int jt, u32x4 (&kr)[LPT], u32x4 (&vr)[LPT]) {
+  // Tiles reach LDS through registers: the loads of tile jt + 2 are issued
+  // in iteration jt and written to the ring (stage (jt + 2) % NSTAGE,
+  // swizzled) at the start of iteration jt + 1. Thread t moves chunks
+  // t, t + THREADS, ... of the tile (16 bytes each).
+  constexpr int CH = (BN * CPR + C::THREADS - 1) / C::THREADS;  // chunks per thread (K or V)
+  u32x4 stk[CH], stv[CH];
+  auto load_tile = [&](int jt) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int qi = i * 256 + threadIdx.x;
-      const int key = min(jt * BN + qi / CPR, kend - 1);
-      const int64_t off = key * kvstride + 8 * (qi % CPR);
-      kr[i] = ld16(kbase + off);
-      vr[i] = ld16(vbase + off);
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      const int r = q / CPR, c = q % CPR;
+      const int64_t off = (int64_t)min(jt * BN + r, kend - 1) * kvstride + 8 * c;
+      stk[i] = ld16(kbase + off);
+      stv[i] = ld16(vbase + off);
+    }
+  };
+  auto store_tile = [&](int jt) {
+    uint8_t* sk_ = lds + (jt % NSTAGE) * 2 * C::TILE_BYTES;
+    uint8_t* sv_ = sk_ + C::TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      const int r = q / CPR, c = q % CPR;
+      *reinterpret_cast<u32x4*>(sk_ + r * D * 2 + swz_rows<D>(r, c) * 16) = stk[i];
+      *reinterpret_cast<u32x4*>(sv_ + r * D * 2 + swz_tr32<D>(r, c) * 16) = stv[i];
     }
   };
 
-  u32x4 kr[LPT], vr[LPT];
-  if (ntiles > 0) load_tile(0, kr, vr);
-  for (int jt = 0; jt < ntiles; ++jt) {
-    if (jt > 0) __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int qi = i * 256 + threadIdx.x;
-      const int r = qi / CPR, c = qi % CPR;
-      *reinterpret_cast<u32x4*>(lk + r * D * 2 + swz_rows<D>(r, c) * 16) = kr[i];
-      *reinterpret_cast<u32x4*>(lv + r * D * 2 + swz_tr32<D>(r, c) * 16) = vr[i];
-    }
-    __syncthreads();
-    if (jt + 1 < ntiles) load_tile(jt + 1, kr, vr);
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  if (ntiles > 1) load_tile(1);
 
+  // The two halves of tile jt: h1 = S^T = K Q^T + online softmax (leaves
+  // bf16 P in pk), h2 = O^T += V^T P^T.
+  u32x4 pk[RB][2][2];
+  auto h1 = [&](int jt) {
+    const uint8_t* lk = lds + (jt % NSTAGE) * 2 * C::TILE_BYTES;
     const int key0 = jt * BN;
-    // ---- S^T = K Q^T: two 32-key blocks
-    f32x16 sacc[2];
+    // ---- S^T = K Q^T: two 32-key blocks x RB row blocks (K read once)
+    f32x16 sacc[RB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-      const int r = 32 * kb + (lane & 31);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+        for (int j = 0; j < 16; ++j) sacc[rb][kb][j] = 0.f;
+    // K fragments stream from LDS PF k-steps ahead of the MFMAs that use
+    // them (the scheduling barriers keep the compiler from pulling the reads
+    // back next to their MFMAs, which would expose the LDS latency each step)
+    constexpr int PF = KS < 4 ? KS : 4;
+    bf16x8 kx[2][KS];
+    auto read_k = [&](int ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = 32 * kb + (lane & 31);
         const int c = 2 * ks + (lane >> 5);
-        const u32x4 kx = *reinterpret_cast<const u32x4*>(lk + r * D * 2 + swz_rows<D>(r, c) * 16);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kx), qv[ks],
-                                                           sacc[kb], 0, 0, 0);
+        kx[kb][ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(lk + r * D * 2 + swz_rows<D>(r, c) * 16));
       }
+    };
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) read_k(ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) read_k(ks + PF);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[rb][kb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx[kb][ks], qv[rb][ks], sacc[rb][kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- online softmax (lane: row `row`, keys key0 + 32 kb + 8 (i/4) + 4 (lane>>5) + i%4)
-    const bool need_mask = key0 + BN > kfull;
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = sacc[kb][i] * a.c;
-        if (need_mask) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (key > row_lim || key >= Lk) x = kNegInf;
-        }
-        sacc[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, xor_lane(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float msub = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - msub);
-    m = mnew;
-    float psum = 0.f;
-    u32x4 pk[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(sacc[kb][8 * h + 2 * j] - msub);
-          const float p1 = fast_exp2(sacc[kb][8 * h + 2 * j + 1] - msub);
-          psum += p0 + p1;
-          pk[kb][h][j] = pack_bf16x2(p0, p1);
-        }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) o[i] *= alpha;
 
-    // ---- O^T += V^T P^T: k-steps (kb, h) of 16 keys each
-    const int g = lane >> 4, m16 = lane & 15;
+    // ---- online softmax per row block (lane: one row; keys
+    //      key0 + 32 kb + 8 (i/4) + 4 (lane>>5) + i%4)
+    const bool need_mask = key0 + BN > kfull;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int rb = 0; rb < RB; ++rb) {
+      if (need_mask) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 pt = __builtin_bit_cast(bf16x8, pk[kb][h]);
-        const int r1 = 32 * kb + 16 * h + 4 * (g >> 1) + (m16 >> 2);
-        const int r2 = r1 + 8;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int col = 32 * db + 16 * (g & 1) + 4 * (m16 & 3);
-          const int ch = col >> 3, half = (col >> 2) & 1;
-          const bf16x4 x1 = lds_read_tr(lv + r1 * D * 2 + swz_tr32<D>(r1, ch) * 16 + half * 8);
-          const bf16x4 x2 = lds_read_tr(lv + r2 * D * 2 + swz_tr32<D>(r2, ch) * 16 + half * 8);
-          const bf16x8 vt = __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pt, o[db], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (key > row_lim[rb] || key >= Lk) sacc[rb][kb][i] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][kb][i]);
+      mx = fmaxf(mx, xor_lane(mx, 32)) * a.c;   // row max in base-2 units
+      // raise the reference max only when the row max grew by more than 2^8
+      // (or the row had no reference yet); rescale O and l when it moves
+      const bool grow = mx > m[rb] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mnew = grow ? mx : m[rb];
+        const float alpha = fast_exp2(m[rb] - mnew);  // m = -inf -> 0
+        if (grow) {
+          m[rb] = mnew;
+          l[rb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < DBLK; ++i) o[rb][i] *= alpha;
         }
       }
+      const float msub = (m[rb] == kNegInf) ? 0.f : m[rb];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j], a.c, -msub));
+            const float p1 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j + 1], a.c, -msub));
+            psum += p0 + p1;
+            pk[rb][kb][h][j] = pack_bf16x2(p0, p1);
+          }
+      l[rb] += psum;
+    }
+
+  };
+  auto h2 = [&](int jt) {
+    const uint8_t* lv = lds + (jt % NSTAGE) * 2 * C::TILE_BYTES + C::TILE_BYTES;
+    // ---- O^T += V^T P^T: k-steps (kb, h) of 16 keys; V^T read once for all
+    //      row blocks
+    // V^T fragments for the 4 k-steps (kb, h) stream from LDS one k-step
+    // ahead of their MFMAs
+    const int g = lane >> 4, m16 = lane & 15;
+    bf16x8 vt[4][DBLK];
+    auto read_v = [&](int step) {
+      const int kb = step >> 1, h = step & 1;
+      const int r1 = 32 * kb + 16 * h + 4 * (g >> 1) + (m16 >> 2);
+      const int r2 = r1 + 8;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const int col = 32 * db + 16 * (g & 1) + 4 * (m16 & 3);
+        const int ch = col >> 3, half = (col >> 2) & 1;
+        const bf16x4 x1 = lds_read_tr(lv + r1 * D * 2 + swz_tr32<D>(r1, ch) * 16 + half * 8);
+        const bf16x4 x2 = lds_read_tr(lv + r2 * D * 2 + swz_tr32<D>(r2, ch) * 16 + half * 8);
+        vt[step][db] = __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    read_v(0);
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      if (step + 1 < 4) read_v(step + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              vt[step][db], __builtin_bit_cast(bf16x8, pk[rb][step >> 1][step & 1]), o[rb][db],
+              0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Ring use: at the start of iteration jt (after the barrier) tile jt + 1
+  // is written into the stage tile jt - 1 used, whose readers all passed the
+  // barrier, and the global loads of tile jt + 2 are issued.
+  for (int jt = 0; jt < ntiles; ++jt) {
+    __syncthreads();
+    if (jt + 1 < ntiles) {
+      store_tile(jt + 1);
+      if (jt + 2 < ntiles) load_tile(jt + 2);
+    }
+    h1(jt);
+    h2(jt);
   }
 
   // ---- epilogue: lane holds O^T[d = 32 db + 8 (i/4) + 4 (lane>>5) + i%4][row]
-  l += xor_lane(l, 32);
-  if (!row_ok) return;
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
-  uint16_t* op = a.out + ((int64_t)(sq.start + tok) * a.Hq + hq) * D + 4 * (lane >> 5);
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float lt = l[rb] + xor_lane(l[rb], 32);
+    if (!row_ok[rb]) continue;
+    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+    uint16_t* op = a.out + ((int64_t)(sq.start + tok[rb]) * a.Hq + hq[rb]) * D + 4 * (lane >> 5);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      u32x2 wv;
-      wv[0] = pack_bf16x2(o[db][4 * i4 + 0] * inv, o[db][4 * i4 + 1] * inv);
-      wv[1] = pack_bf16x2(o[db][4 * i4 + 2] * inv, o[db][4 * i4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i4) = wv;
-    }
-  if ((lane >> 5) == 0)
-    a.lse[(int64_t)(sq.start + tok) * a.Hq + hq] = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : kNegInf;
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        u32x2 wv;
+        wv[0] = pack_bf16x2(o[rb][db][4 * i4 + 0] * inv, o[rb][db][4 * i4 + 1] * inv);
+        wv[1] = pack_bf16x2(o[rb][db][4 * i4 + 2] * inv, o[rb][db][4 * i4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i4) = wv;
+      }
+    if ((lane >> 5) == 0)
+      a.lse[(int64_t)(sq.start + tok[rb]) * a.Hq + hq[rb]] =
+          (lt > 0.f) ? (m[rb] + fast_log2(lt)) * kLn2 : kNegInf;
+  }
 }
 
 template <int D>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int grid, hipStream_t st) {
-  prefill_kernel<D><<<grid, 256, 0, st>>>(a);
+  prefill_kernel<D><<<grid, PrefillCfg<D>::THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
+
+static_assert(PrefillCfg<32>::ROWS == prefill_rows(32) && PrefillCfg<64>::ROWS == prefill_rows(64) &&
+                  PrefillCfg<128>::ROWS == prefill_rows(128) &&
+                  PrefillCfg<256>::ROWS == prefill_rows(256),
+              "plan and kernel disagree on the prefill tile");
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st) {
   switch (D) {
