@@ -135,7 +135,19 @@ def long_decode(args):
         k, v = ks[i], vs[i]
         fns.append(lambda k=k, v=v: plan(q, k, v, cu_q, cu_kv, out=out, lse=lse, B=B))
     graphs = [capture(f) for f in fns]
-    total, _ = time_replays([g.replay for g in graphs], args.steps, args.warmup)
+    gsteps = args.graph_steps if args.graph_steps > 0 else ncopy
+    if gsteps > 1:
+        # one graph holds gsteps consecutive steps (one per K/V copy, in turn),
+        # as a model's captured forward holds one attention call per layer
+        group = capture(lambda: [fns[i % ncopy]() for i in range(gsteps)])
+        seq = [group.replay] * (args.steps // gsteps) + \
+              [graphs[i % ncopy].replay for i in range(args.steps % gsteps)]
+        for i in range(max(1, args.warmup // gsteps)):
+            group.replay()
+        torch.cuda.synchronize()
+        total, _ = time_replays(seq, len(seq), 0)
+    else:
+        total, _ = time_replays([g.replay for g in graphs], args.steps, args.warmup)
     _, per = time_replays(fns, max(50, min(args.steps, 400)), 5)
     ms = total / args.steps
     alg_bytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4   # K+V, Q, O, LSE
@@ -150,7 +162,7 @@ def long_decode(args):
         ms_per_step=round(ms, 5), us_per_step=round(ms * 1e3, 2),
         kv_bytes_per_step=kv_bytes, frac_hbm_peak=round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         config=dict(workload="long decode: B=1, Hq=64, Hkv=8, D=128, Lk=32768, bf16 THD, "
-                             f"{ncopy} rotating K/V copies (MALL defeat), graph replay",
+                             f"{ncopy} rotating K/V copies (MALL defeat), graphs of {gsteps} step(s)",
                     B=B, Hq=Hq, Hkv=Hkv, D=D, kv_len=L, nsplit=info["nsplit"],
                     decode_path=("mfma" if info["decode_path"] == 2 else "wave"),
                     grid=info["grid"], threads=info["threads"],
@@ -340,6 +352,8 @@ def main():
     ap.add_argument("--prefill-len", type=int, default=0,
                     help="with --workload prefill: give every sequence this length")
     ap.add_argument("--decode-waves", type=int, default=0, choices=[0, 4, 8])
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="long decode: steps per captured graph (0 = one per K/V copy)")
     ap.add_argument("--workload", default="long_decode",
                     choices=["long_decode", "prefill", "batched_decode"],
                     help="headline workload (default: long decode); the others are for "

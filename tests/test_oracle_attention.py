@@ -60,6 +60,32 @@ def test_matches_scalar_brute_force(seed):
     assert np.isnan(out[~written]).all() and np.isnan(lse[~written]).all()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_selected_rows_match_scalar_brute_force(seed):
+    """attend_selected (the row-at-a-time form used to sample large workloads)
+    against the scalar triple loops, on every (sequence, query, head) triple
+    of a tiny ragged pack, causal and not, with Lq != Lk."""
+    rng = np.random.default_rng([8, seed])
+    Hkv, G = int(rng.choice([1, 2])), int(rng.choice([1, 3]))
+    Hq, D, B = Hkv * G, int(rng.choice([3, 8])), int(rng.integers(1, 4))
+    causal = bool(seed % 2)
+    q, k, v, cu_q, cu_k = _rand_case(rng, B, Hq, Hkv, D, 5, 7, causal, lead=1, tail=2)
+    ref = brute.attend_scalar(q.tolist(), k.tolist(), v.tolist(), cu_q, cu_k, B, causal)
+    picks = [(b, i, h) for b in range(B) for i in range(int(cu_q[b + 1] - cu_q[b]))
+             for h in range(Hq)]
+    picks = [picks[j] for j in rng.permutation(len(picks))]
+    got = A.attend_selected(q, k, v, cu_q, cu_k, causal, picks)
+    assert len(got) == len(picks) == len(ref)
+    for (b, i, h), (row, hh, o, ls) in zip(picks, got):
+        assert (row, hh) == (int(cu_q[b]) + i, h)
+        ro, rl = ref[(row, h)]
+        np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-12)
+        if math.isinf(rl):
+            assert ls == -np.inf and not o.any()
+        else:
+            assert abs(ls - rl) <= 1e-12 * max(1.0, abs(rl))
+
+
 def _sdpa_reference(q, k, v, cu_q, cu_k, B, causal):
     """PyTorch CPU fp64: SDPA with an explicit boolean mask, GQA expanded to
     MHA by repeating each KV head G times (head h reads KV head h // G)."""

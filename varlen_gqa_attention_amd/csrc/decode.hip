@@ -5,11 +5,12 @@
 // of each (sequence, kv head) is cut into `nsplit` contiguous chunks that run
 // on separate workgroups; each emits an unnormalised partial (O, m, l) and a
 // log-sum-exp merge combines them. With one split the same workgroup
-// normalises and writes the output directly. The merge runs either in a
-// separate combine kernel or, by default, inside the split kernel: the last
-// split workgroup of a unit to finish (a device-scope counter, reset by that
-// workgroup so the next launch or graph replay starts from zero) merges the
-// unit's partials, which saves a launch and the combine kernel's round trips.
+// normalises and writes the output directly. By default the merge is a
+// separate combine kernel. A plan option moves it into the split kernel: the
+// last split workgroup of a unit to finish (a system-scope counter, reset by
+// that workgroup so the next launch or graph replay starts from zero) merges
+// the unit's partials, which saves a launch but needs write-through partial
+// stores and cache-bypassing reads; it measures no faster on gfx950.
 //
 // Workgroup = (sequence b, kv head hk, head block hb, split s). Its waves take
 // the 32-key tiles of the chunk round-robin, keep their own running
@@ -78,6 +79,38 @@ __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
   return u;
 }
 
+// Drives one wave's tiles w, w + NW, ... (fewer than ntiles in all) through
+// two register buffers, A holding tile t and B tile t + NW, so two tiles are
+// in flight. Every load in the steady-state loop is unconditional, so the
+// number of loads outstanding at each wait is the same on all paths and a
+// wait covers only the tile it needs; the last one to three tiles run in
+// straight-line tails that issue no further loads (B re-reads tile w only
+// when the wave has a single tile).
+template <int NW, typename Buf, typename Load, typename Proc>
+__device__ __forceinline__ void pipeline_tiles(int w, int ntiles, Buf& A, Buf& B, Load load,
+                                               Proc proc) {
+  if (w >= ntiles) return;
+  const int nt = (ntiles - 1 - w) / NW + 1;
+  load(w, A);
+  load(w + (nt > 1 ? NW : 0), B);
+  int t = w, left = nt;
+  for (; left > 3; left -= 2, t += 2 * NW) {
+    proc(t, A);
+    load(t + 2 * NW, A);
+    proc(t + NW, B);
+    load(t + 3 * NW, B);
+  }
+  if (left == 3) {
+    proc(t, A);
+    load(t + 2 * NW, A);
+    proc(t + NW, B);
+    proc(t + 2 * NW, A);
+  } else {
+    proc(t, A);
+    if (left == 2) proc(t + NW, B);
+  }
+}
+
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int qrow, int hq, int d, float val) {
   __bf16 ob = (__bf16)val;
   a.out[((int64_t)qrow * a.Hq + hq) * a.D + d] = __builtin_bit_cast(uint16_t, ob);
@@ -106,97 +139,123 @@ __device__ __forceinline__ void st_part(float* p, float v) {
   else *p = v;
 }
 
-// LSE merge of the first n_live split partials of heads [h0, h0 + nh) of
-// sequence b, written as bf16 out and fp32 LSE. Used by the combine kernel
-// and by the fused merge, with the same arithmetic order in both. All of a
-// thread's partial loads are issued before the first is used.
-template <int D, bool COHERENT>
-__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int qrow, int h0, int nh,
-                                               int n_live) {
+// LSE merge of split partials of heads [h0, h0 + nh) of sequence b, written
+// as bf16 out and fp32 LSE; one thread per (head, d), nh * D <= blockDim.x.
+// Used by the combine kernel and by the fused merge, with the same arithmetic
+// in both. Slots are taken in chunks of 32: lane j of each 32-lane half loads
+// slot s0 + j's (m, l) (a half never spans two heads, since D >= 32), the
+// chunk max and the weighted l sum are half-wave reductions, and the weights
+// reach every lane of the half by readlane for the O sum. The first chunk's
+// loads (slots clamped to the allocated nsplit) are issued before `lens()`
+// runs, so the combine kernel reads cu_seqlens while its partials are in
+// flight; lens() returns {query row, n_live}, or n_live < 0 to write nothing.
+// Slots at or past n_live may hold stale values from another launch and are
+// excluded with selects (never multiplied by a zero weight, which would keep
+// a NaN). Chunks after the first merge online (running max, rescaled sums).
+struct MergeTarget {
+  int qrow, n_live;
+};
+
+template <int D, bool COHERENT, typename Lens>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h0, int nh, Lens lens) {
+  static_assert(D >= 32, "a 32-lane half must not span two heads");
   const float* pml = reinterpret_cast<const float*>(a.part_ml);
   constexpr int CH = 32;
-  for (int idx = threadIdx.x; idx < nh * D; idx += blockDim.x) {
-    const int h = idx / D, d = idx % D;
-    const int hq = h0 + h;
-    const int64_t base = (int64_t)(b * a.Hq + hq) * a.nsplit;
-    // loads are unconditional (indices clamped to the last live split) so a
-    // chunk's loads are all in flight at once; extra slots get weight 0
-    float M = kNegInf;
-    for (int s0 = 0; s0 < n_live; s0 += CH) {
-      float mv[CH];
+  const int idx = threadIdx.x;
+  const int lane = idx & 63, sl = lane & 31;
+  const int h = idx / D, d = idx % D;
+  const int hq = h0 + min(h, nh - 1);
+  const int64_t base = (int64_t)(b * a.Hq + hq) * a.nsplit;
+  float ms, ls, po[CH];
+  auto load_chunk = [&](int s0, int n_slots) {
+    const int64_t si = base + min(s0 + sl, n_slots - 1);
+    ms = ld_part<COHERENT>(pml + 2 * si);
+    ls = ld_part<COHERENT>(pml + 2 * si + 1);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) mv[j] = ld_part<COHERENT>(pml + 2 * (base + min(s0 + j, n_live - 1)));
+    for (int j = 0; j < CH; ++j)
+      po[j] = ld_part<COHERENT>(a.part_o + (base + min(s0 + j, n_slots - 1)) * D + d);
+  };
+  load_chunk(0, a.nsplit);
+  const MergeTarget tg = lens();
+  if (tg.n_live < 0 || h >= nh) return;  // uniform per 32-lane half
+  float M = kNegInf, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < tg.n_live; s0 += CH) {
+    if (s0 > 0) load_chunk(s0, tg.n_live);
+    const bool live = s0 + sl < tg.n_live;
+    const float Mn = fmaxf(M, group_max<32>(live ? ms : kNegInf));
+    const float Ms = (Mn == kNegInf) ? 0.f : Mn;
+    const float r = fast_exp2(M - Ms);
+    const float wl = live ? fast_exp2(ms - Ms) : 0.f;
+    L = L * r + group_sum<32>(live ? wl * ls : 0.f);
+    O *= r;
 #pragma unroll
-      for (int j = 0; j < CH; ++j) M = fmaxf(M, mv[j]);
+    for (int j = 0; j < CH; ++j) {
+      const float w0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), j));
+      const float w1 =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), 32 + j));
+      const float wj = (lane & 32) ? w1 : w0;
+      O += (s0 + j < tg.n_live) ? wj * po[j] : 0.f;
     }
-    const float Ms = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-    for (int s0 = 0; s0 < n_live; s0 += CH) {
-      float mm[CH], ll[CH], po[CH];
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int64_t sj = base + min(s0 + j, n_live - 1);
-        mm[j] = ld_part<COHERENT>(pml + 2 * sj);
-        ll[j] = ld_part<COHERENT>(pml + 2 * sj + 1);
-        po[j] = ld_part<COHERENT>(a.part_o + sj * D + d);
-      }
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const float wt = (s0 + j < n_live) ? fast_exp2(mm[j] - Ms) : 0.f;
-        L += wt * ll[j];
-        O += wt * po[j];
-      }
-    }
-    store_out(a, qrow, hq, d, (L > 0.f) ? O / L : 0.f);
-    if (d == 0) a.lse[(int64_t)qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+    M = Mn;
   }
+  store_out(a, tg.qrow, hq, d, (L > 0.f) ? O / L : 0.f);
+  if (d == 0) a.lse[(int64_t)tg.qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 // Cross-wave merge of per-wave (m, l, O) states held in LDS, then the
 // epilogue: direct (normalised bf16 out + LSE) or split partial; in fused
 // mode the last split workgroup of the unit then merges all partials.
-// mo: [NW][HPB][D] floats, mm / ml: [NW][HPB].
-template <int D, int NW, int HPB>
+// mo: [NW][HPB][D] floats, mml: [NW][HPB] (m, l) pairs. One thread per
+// (head, 4 consecutive d), so LDS reads and global stores are 8-16 bytes.
+template <int D, int NW, int HPB, bool FUSED>
 __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const UnitCoords& u, int Lk,
                                                  int qrow, int h0, int nh, const float* mo,
-                                                 const float* mm, const float* ml, int* flag) {
-  for (int idx = threadIdx.x; idx < nh * D; idx += NW * 64) {
-    const int h = idx / D, d = idx % D;
+                                                 const float2* mml, int* flag) {
+  constexpr int D4 = D / 4;
+  for (int idx = threadIdx.x; idx < nh * D4; idx += NW * 64) {
+    const int h = idx / D4, d = 4 * (idx % D4);
+    float2 ml[NW];
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * HPB + h]);
+    for (int w = 0; w < NW; ++w) {
+      ml[w] = mml[w * HPB + h];
+      M = fmaxf(M, ml[w].x);
+    }
     const float Ms = (M == kNegInf) ? 0.f : M;
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float wt = fast_exp2(mm[w * HPB + h] - Ms);
-      L += wt * ml[w * HPB + h];
-      O += wt * mo[(w * HPB + h) * D + d];
+      const float wt = fast_exp2(ml[w].x - Ms);
+      L += wt * ml[w].y;
+      O += wt * *reinterpret_cast<const f32x4*>(mo + (w * HPB + h) * D + d);
     }
     const int hq = h0 + h;
     if (a.direct) {
-      store_out(a, qrow, hq, d, (L > 0.f) ? O / L : 0.f);
+      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      u32x2 ov;
+      ov[0] = pack_bf16x2(O[0] * inv, O[1] * inv);
+      ov[1] = pack_bf16x2(O[2] * inv, O[3] * inv);
+      *reinterpret_cast<u32x2*>(a.out + ((int64_t)qrow * a.Hq + hq) * D + d) = ov;
       if (d == 0)
         a.lse[(int64_t)qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
     } else {
       const int64_t pidx = ((int64_t)(u.b * a.Hq + hq) * a.nsplit + u.s);
       float* pml = reinterpret_cast<float*>(a.part_ml);
-      if (a.fused) {
-        st_part<true>(a.part_o + pidx * D + d, O);
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_part<true>(a.part_o + pidx * D + d + i, O[i]);
         if (d == 0) {
           st_part<true>(pml + 2 * pidx, M);
           st_part<true>(pml + 2 * pidx + 1, L);
         }
       } else {
-        st_part<false>(a.part_o + pidx * D + d, O);
-        if (d == 0) {
-          st_part<false>(pml + 2 * pidx, M);
-          st_part<false>(pml + 2 * pidx + 1, L);
-        }
+        *reinterpret_cast<f32x4*>(a.part_o + pidx * D + d) = O;
+        if (d == 0) a.part_ml[pidx] = float2{M, L};
       }
     }
   }
-  if (a.direct || !a.fused) return;
+  if (!FUSED || a.direct) return;
   // Fused merge. The partials above were written through to memory; once
   // every thread's stores have completed (the wait below) the workgroup counts
   // itself in with a system-scope atomic, and the last live split of the unit
@@ -214,13 +273,15 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
   }
   __syncthreads();
   if (!*flag) return;
-  merge_partials<D, true>(a, u.b, qrow, h0, nh, n_live);
+  for (int hc = 0; hc < nh; hc += NW * 64 / D)
+    merge_partials<D, true>(a, u.b, h0 + hc, min(NW * 64 / D, nh - hc),
+                            [&] { return MergeTarget{qrow, n_live}; });
 }
 
 // ---------------------------------------------------------------------------
 // MFMA path
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;     // 32-wide k-steps of Q K^T
   constexpr int DB = D / 16;     // 16-wide d blocks of P V
@@ -246,7 +307,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int nh = min(HPB, a.G - u.hb * HPB);
   const int kbeg = u.s * a.chunk_keys;
   if (!a.direct && kbeg >= Lk) {  // empty split: never merged
-    if (Lk == 0 && u.s == 0 && a.fused) store_empty(a, qrow, h0, nh);
+    if (FUSED && Lk == 0 && u.s == 0) store_empty(a, qrow, h0, nh);
     return;
   }
   const int kend = min(kbeg + a.chunk_keys, Lk);
@@ -360,45 +421,30 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     wave_lds_sync();
   };
 
-  // Two tiles in flight per wave: A holds tile t, B tile t + NW. Loads are
-  // issued unconditionally (past the wave's last tile they re-read that tile,
-  // which the caches still hold) so the number of loads outstanding at every
-  // wait is the same on all paths and each wait covers only the tile it needs.
-  if (w < ntiles) {
-    const int tl = w + NW * ((ntiles - 1 - w) / NW);  // this wave's last tile
-    u32x4 kA[2][KS], vA[DV], kB[2][KS], vB[DV];
-    load_tile(w, kA, vA);
-    load_tile(min(w + NW, tl), kB, vB);
-    for (int t = w; t < ntiles; t += 2 * NW) {
-      process_tile(t, kA, vA);
-      load_tile(min(t + 2 * NW, tl), kA, vA);
-      if (t + NW < ntiles) process_tile(t + NW, kB, vB);
-      load_tile(min(t + 3 * NW, tl), kB, vB);
-    }
-  }
+  struct TileRegs {
+    u32x4 k[2][KS], v[DV];
+  } A, B;
+  pipeline_tiles<NW>(w, ntiles, A, B, [&](int t, TileRegs& r) { load_tile(t, r.k, r.v); },
+                     [&](int t, TileRegs& r) { process_tile(t, r.k, r.v); });
   // l: each lane summed its own 8 keys per tile; add the four key groups
   l += xor_lane(l, 16);
   l += xor_lane(l, 32);
 
   __syncthreads();  // staging area becomes the merge area
   float* mo = reinterpret_cast<float*>(lds);
-  float* mm = mo + NW * HPB * D;
-  float* ml = mm + NW * HPB;
+  float2* mml = reinterpret_cast<float2*>(mo + NW * HPB * D);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
     *reinterpret_cast<f32x4*>(mo + (w * HPB + hl) * D + 16 * db + 4 * g4) = o[db];
-  if (g4 == 0) {
-    mm[w * HPB + hl] = m;
-    ml[w * HPB + hl] = l;
-  }
+  if (g4 == 0) mml[w * HPB + hl] = float2{m, l};
   __syncthreads();
-  finish_workgroup<D, NW, HPB>(a, u, Lk, qrow, h0, nh, mo, mm, ml, &s_flag);
+  finish_workgroup<D, NW, HPB, FUSED>(a, u, Lk, qrow, h0, nh, mo, mml, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
 // Wave (VALU) path for small G
 // ---------------------------------------------------------------------------
-template <int D, int NW, int GM>
+template <int D, int NW, int GM, bool FUSED>
 __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;             // lanes per key row (8 d-values each)
   constexpr int RPI = 64 / LPR;          // key rows per load instruction
@@ -420,7 +466,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   const int nh = min(GM, a.G - u.hb * GM);
   const int kbeg = u.s * a.chunk_keys;
   if (!a.direct && kbeg >= Lk) {
-    if (Lk == 0 && u.s == 0 && a.fused) store_empty(a, qrow, h0, nh);
+    if (FUSED && Lk == 0 && u.s == 0) store_empty(a, qrow, h0, nh);
     return;
   }
   const int kend = min(kbeg + a.chunk_keys, Lk);
@@ -515,9 +561,13 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
     }
   };
 
-  if (w < ntiles) {  // two tiles in flight, unconditional loads (see the MFMA path)
+  u32x4 kA[NI], vA[NI], kB[NI], vB[NI];
+  // Two tiles in flight with unconditional loads, as in pipeline_tiles, but
+  // one loop: past the wave's last tile the loads re-read that tile (cached).
+  // This path runs long sequences (many tiles per wave), where the re-reads
+  // are negligible, and the compact loop keeps register use low.
+  if (w < ntiles) {
     const int tl = w + NW * ((ntiles - 1 - w) / NW);
-    u32x4 kA[NI], vA[NI], kB[NI], vB[NI];
     load_tile(w, kA, vA);
     load_tile(min(w + NW, tl), kB, vB);
     for (int t = w; t < ntiles; t += 2 * NW) {
@@ -535,8 +585,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) o[g][j] = across_groups_sum<LPR>(o[g][j]);
   }
   float* mo = lds;
-  float* mm = mo + NW * GM * D;
-  float* ml = mm + NW * GM;
+  float2* mml = reinterpret_cast<float2*>(mo + NW * GM * D);
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
@@ -548,13 +597,10 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      mm[w * GM + g] = m[g];
-      ml[w * GM + g] = l[g];
-    }
+    for (int g = 0; g < GM; ++g) mml[w * GM + g] = float2{m[g], l[g]};
   }
   __syncthreads();
-  finish_workgroup<D, NW, GM>(a, u, Lk, qrow, h0, nh, mo, mm, ml, &s_flag);
+  finish_workgroup<D, NW, GM, FUSED>(a, u, Lk, qrow, h0, nh, mo, mml, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,11 +610,11 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
   if (b >= a.B) return;
-  const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
-  if (sq.len == 0) return;
-  const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
-  const int n_live = (sk.len + a.chunk_keys - 1) / a.chunk_keys;
-  merge_partials<D, false>(a, b, sq.start, h, 1, n_live);
+  merge_partials<D, false>(a, b, h, 1, [&] {
+    const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
+    const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
+    return MergeTarget{sq.start, sq.len == 0 ? -1 : (sk.len + a.chunk_keys - 1) / a.chunk_keys};
+  });
 }
 
 __global__ void clear_words_kernel(int32_t* w, int n) {
@@ -578,16 +624,26 @@ __global__ void clear_words_kernel(int32_t* w, int n) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+template <int D, bool FUSED>
+static void launch_split(const DecodeArgs& a, int path, int nw, int grid, hipStream_t st) {
+  // 8-wave workgroups only for D <= 128 (the plan never picks them above)
+  if constexpr (D <= 128) {
+    if (nw == 8) {
+      if (path == 2) decode_mfma_kernel<D, 8, FUSED><<<grid, 512, 0, st>>>(a);
+      else decode_wave_kernel<D, 8, 4, FUSED><<<grid, 512, 0, st>>>(a);
+      return;
+    }
+  }
+  if (path == 2) decode_mfma_kernel<D, 4, FUSED><<<grid, 256, 0, st>>>(a);
+  else decode_wave_kernel<D, 4, 4, FUSED><<<grid, 256, 0, st>>>(a);
+}
+
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
                                   hipStream_t st) {
-  if (path == 2) {
-    if (nw == 8) decode_mfma_kernel<D, 8><<<grid, 512, 0, st>>>(a);
-    else decode_mfma_kernel<D, 4><<<grid, 256, 0, st>>>(a);
-  } else {
-    if (nw == 8) decode_wave_kernel<D, 8, 4><<<grid, 512, 0, st>>>(a);
-    else decode_wave_kernel<D, 4, 4><<<grid, 256, 0, st>>>(a);
-  }
+  // the fused-merge code is compiled only into the kernels that use it
+  if (a.fused && !a.direct) launch_split<D, true>(a, path, nw, grid, st);
+  else launch_split<D, false>(a, path, nw, grid, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.fused) return e;
   decode_combine_kernel<D><<<combine_grid, D < 64 ? 64 : D, 0, st>>>(a);

@@ -65,6 +65,18 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Max over aligned groups of N lanes (N in 1..64), as group_sum.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
+  if constexpr (N >= 32) x = fmaxf(x, xor_lane(x, 16));
+  if constexpr (N >= 64) x = fmaxf(x, xor_lane(x, 32));
+  return x;
+}
+
 // Max / sum across lanes that differ only in the bits of [FROM, 64): combines
 // the aligned groups of FROM lanes that hold the same element.
 template <int FROM>

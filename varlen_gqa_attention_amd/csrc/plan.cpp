@@ -79,15 +79,16 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     const int64_t grid = (int64_t)in.n_units * nsplit;
     if (grid > (1LL << 31) - 1) return VATTN_ERR_UNSUPPORTED;
     in.grid = (int)grid;
-    // one wave per tile of the chunk, up to 8; 8 waves when at most one
-    // workgroup lands on each CU so that a lone workgroup keeps enough bytes
-    // in flight.
+    // 4 waves per workgroup. The wave path takes 8 when at most one
+    // workgroup lands on each CU, so that a lone workgroup keeps enough bytes
+    // in flight; the MFMA path measured faster with 4 in that case too (its
+    // waves hold two 32-key tiles each, and the cross-wave merge halves).
     // (D = 256 stays at 4 waves: 8 would exceed the register file.)
-    in.threads = (in.grid <= n_cu && D <= 128) ? 512 : 256;
+    in.threads = (in.grid <= n_cu && D <= 128 && in.decode_path == 1) ? 512 : 256;
     if (o.decode_waves == 4 || (o.decode_waves == 8 && D <= 128)) in.threads = 64 * o.decode_waves;
     // the merge runs in a separate combine kernel unless the in-kernel merge
-    // is asked for (on this chip the two cost about the same: the in-kernel
-    // merge saves a launch but serialises write-through, atomic and reads)
+    // is asked for (on this chip the in-kernel merge is slower: it saves a
+    // launch but serialises write-through stores, an atomic and the reads)
     in.fused_combine = (!in.direct && o.fuse_combine == 1) ? 1 : 0;
     in.combine_grid = (in.direct || in.fused_combine) ? 0 : B_max * Hq;
     in.scratch_bytes = 256;  // error word, aligned

@@ -23,6 +23,7 @@ int main() {
   CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.is_decode && in.nsplit == 32 && in.grid == 256 && in.chunk_keys == 1024 && !in.direct);
   CHECK(in.decode_path == VATTN_DECODE_MFMA && in.fused_combine == 0 && in.combine_grid == 64);
+  CHECK(in.threads == 256);
   {
     vattn_plan_opts fu = {};
     fu.fuse_combine = 1;  // in-kernel merge: no combine launch
@@ -32,9 +33,13 @@ int main() {
   // batch * kv heads fills the device: direct write
   CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0 && in.decode_path == VATTN_DECODE_WAVE);
-  // prefill grid from B_max and s_max_q, G heads folded into 128 rows
+  // prefill grid from B_max and s_max_q, G heads folded into 256 rows (D <= 128)
   CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 128, 1, nullptr, 256, &in) == VATTN_OK);
-  CHECK(!in.is_decode && in.q_tokens_per_tile == 32 && in.n_qtiles == 128 && in.grid == 16384);
+  CHECK(!in.is_decode && in.q_tokens_per_tile == 64 && in.n_qtiles == 64 && in.grid == 8192);
+  CHECK(in.threads == 512);
+  // D = 256: 128 rows, 4 waves
+  CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 256, 1, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.q_tokens_per_tile == 32 && in.n_qtiles == 128 && in.grid == 16384 && in.threads == 256);
   // validation
   CHECK(vattn::plan_compute(1, 1, 64, 6, 4, 64, 0, nullptr, 256, &in) == VATTN_ERR_INVALID_ARG);
   CHECK(vattn::plan_compute(1, 1, 64, 8, 2, 80, 0, nullptr, 256, &in) == VATTN_ERR_UNSUPPORTED);
