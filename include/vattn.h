@@ -210,6 +210,21 @@ vattn_status vattn_plan_read_error(vattn_plan_t p, int32_t* value);
 /* Enqueue a reset of the error word to 0 on `stream` (a kernel, no memset). */
 vattn_status vattn_plan_clear_error(vattn_plan_t p, vattn_stream_t stream);
 
+/*
+ * Measurement hook (profiling, not part of the attention computation). With
+ * both handles non-NULL, every later vattn_execute / vattn_execute_exact_grid
+ * on this plan launches its main kernel (the split or direct decode kernel,
+ * or the prefill kernel) with `start` and `stop` stamped at the start and end
+ * of that kernel's dispatch (hipExtLaunchKernelGGL), so that the elapsed time
+ * between them is that kernel's duration; a combine kernel that follows is
+ * not included. The handles are hipEvent_t values
+ * created and owned by the caller, who keeps them alive until that work is
+ * done; NULL, NULL turns the hook off. While the hook is set, execute on a
+ * capturing stream returns VATTN_ERR_INVALID_ARG (events are not recorded into
+ * graphs). Host-only call: no device work, no synchronisation.
+ */
+vattn_status vattn_plan_set_kernel_events(vattn_plan_t p, void* start, void* stop);
+
 /* Free the plan's scratch. Safe on NULL. Work already enqueued must be done. */
 void vattn_plan_destroy(vattn_plan_t p);
 

@@ -80,3 +80,37 @@ def test_rows_past_capacity_are_cut_and_flagged():
     ref_o, ref_l, _ = A.attend_varlen(I.bf16_to_f64(q), I.bf16_to_f64(k), I.bf16_to_f64(k),
                                       [0, 1, 2], [0, 30, 50], 2, False)
     assert_out_close(I.bf16_to_f64(out), ref_o)
+
+
+def test_kernel_event_hook():
+    """The measurement hook records its events around the main kernel only,
+    leaves results unchanged, and rejects a half-set pair."""
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import _lib
+    L = _lib.load()
+    B, Hq, Hkv, D, Lk = 1, 16, 2, 64, 4096
+    plan = V.Plan(B, 1, Lk, Hq, Hkv, D, False, force_nsplit=8)
+    q = I.normal_bf16((B, Hq, D), 41, "cuda")
+    k = I.normal_bf16((Lk, Hkv, D), 42, "cuda")
+    v = I.normal_bf16((Lk, Hkv, D), 43, "cuda")
+    cu_q = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    cu_kv = torch.tensor([0, Lk], dtype=torch.int32, device="cuda")
+    out0, lse0 = plan(q, k, v, cu_q, cu_kv)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with pytest.raises(ValueError):
+        plan.set_kernel_events(a, b)                       # not yet created
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    assert L.vattn_plan_set_kernel_events(plan._h, ctypes.c_void_p(a.cuda_event), None) == -1
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    plan.set_kernel_events(a, b)
+    t0.record()
+    out1, lse1 = plan(q, k, v, cu_q, cu_kv)
+    t1.record()
+    plan.set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    kern, whole = a.elapsed_time(b), t0.elapsed_time(t1)
+    assert 0.0 < kern <= whole
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)

@@ -141,6 +141,20 @@ class Plan:
         _lib.check(_LIB.vattn_plan_clear_error(self._h, ctypes.c_void_p(s.cuda_stream)),
                    "vattn_plan_clear_error")
 
+    def set_kernel_events(self, start=None, stop=None):
+        """Measurement hook: record the torch.cuda.Event pair `start` / `stop`
+        around the plan's main kernel in later eager calls (None, None: off).
+        The events must already have been recorded once (torch creates the
+        underlying HIP event lazily, on first record)."""
+        if (start is None) != (stop is None):
+            raise ValueError("give both events or neither")
+        hs = [ctypes.c_void_p(e.cuda_event if e is not None else 0) for e in (start, stop)]
+        if start is not None and not (hs[0].value and hs[1].value):
+            raise ValueError("record each event once before passing it")
+        _lib.check(_LIB.vattn_plan_set_kernel_events(self._h, hs[0], hs[1]),
+                   "vattn_plan_set_kernel_events")
+        self._events = (start, stop)  # keep them alive while the hook is set
+
     def close(self):
         if self._h:
             _LIB.vattn_plan_destroy(self._h)

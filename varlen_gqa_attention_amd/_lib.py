@@ -25,7 +25,8 @@ EXPORTS = (
     "vattn_status_string", "vattn_abi_version", "vattn_plan", "vattn_plan_ex",
     "vattn_plan_describe", "vattn_plan_query", "vattn_execute",
     "vattn_execute_exact_grid", "vattn_padding_mask", "vattn_plan_error_word",
-    "vattn_plan_read_error", "vattn_plan_clear_error", "vattn_plan_destroy",
+    "vattn_plan_read_error", "vattn_plan_clear_error", "vattn_plan_set_kernel_events",
+    "vattn_plan_destroy",
 )
 
 
@@ -97,6 +98,8 @@ def load():
     L.vattn_plan_read_error.argtypes = [vp, i32p]
     L.vattn_plan_clear_error.restype = c_int
     L.vattn_plan_clear_error.argtypes = [vp, vp]
+    L.vattn_plan_set_kernel_events.restype = c_int
+    L.vattn_plan_set_kernel_events.argtypes = [vp, vp, vp]
     L.vattn_plan_destroy.restype = None
     L.vattn_plan_destroy.argtypes = [vp]
     _lib = L

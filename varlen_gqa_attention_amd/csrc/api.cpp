@@ -21,6 +21,7 @@ struct vattn_plan_s {
   int32_t* counters;
   float2* part_ml;
   float* part_o;
+  hipEvent_t ev_start, ev_stop;  // measurement hook (caller-owned), or null
 };
 
 namespace {
@@ -151,6 +152,11 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
   const float c = (float)(1.0 / std::sqrt((double)in.D) * 1.4426950408889634);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
+  if (p->ev_start) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return VATTN_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return VATTN_ERR_INVALID_ARG;
+  }
   if (in.is_decode) {
     vattn::DecodeArgs a;
     a.q = (const uint16_t*)q;
@@ -180,7 +186,7 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.direct = in.direct;
     a.fused = in.fused_combine;
     e = vattn::launch_decode(a, in.decode_path, in.threads / 64, in.grid, in.combine_grid,
-                             st);
+                             st, p->ev_start, p->ev_stop);
   } else {
     vattn::PrefillArgs a;
     a.q = (const uint16_t*)q;
@@ -209,7 +215,7 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     const int64_t grid = tile_map ? (int64_t)n_map * in.Hkv : in.grid;
     if (grid == 0) return VATTN_OK;
     if (grid > INT32_MAX) return VATTN_ERR_UNSUPPORTED;
-    e = vattn::launch_prefill(a, in.D, (int)grid, st);
+    e = vattn::launch_prefill(a, in.D, (int)grid, st, p->ev_start, p->ev_stop);
   }
   return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
 }
@@ -243,6 +249,13 @@ vattn_status vattn_padding_mask(const int32_t* cu_seqlens, int B, int max_seqlen
   if (!cu_seqlens || !mask || !aligned(cu_seqlens, 4)) return VATTN_ERR_INVALID_ARG;
   hipError_t e = vattn::launch_padding_mask(cu_seqlens, B, max_seqlen, mask, (hipStream_t)stream);
   return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
+}
+
+vattn_status vattn_plan_set_kernel_events(vattn_plan_t p, void* start, void* stop) {
+  if (!p || (!start) != (!stop)) return VATTN_ERR_INVALID_ARG;
+  p->ev_start = (hipEvent_t)start;
+  p->ev_stop = (hipEvent_t)stop;
+  return VATTN_OK;
 }
 
 const int32_t* vattn_plan_error_word(vattn_plan_t p) { return p ? p->err : nullptr; }

@@ -33,6 +33,8 @@
 //  * Wave: for small G (GEMV-shaped work) each 16-byte load lane holds 8
 //    d-values of one key; dot products use v_dot2_f32_bf16 and DPP row
 //    reductions; P V is plain FMAs.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -624,26 +626,37 @@ __global__ void clear_words_kernel(int32_t* w, int n) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// With a measurement event pair the kernel is launched through
+// hipExtLaunchKernelGGL, which stamps the events with the dispatch's own start
+// and end (no separate event packets around it).
+template <typename Kern>
+static void launch_timed(Kern kern, int grid, int threads, hipStream_t st, hipEvent_t ev0,
+                         hipEvent_t ev1, const DecodeArgs& a) {
+  if (ev0) hipExtLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, st, ev0, ev1, 0, a);
+  else kern<<<grid, threads, 0, st>>>(a);
+}
+
 template <int D, bool FUSED>
-static void launch_split(const DecodeArgs& a, int path, int nw, int grid, hipStream_t st) {
+static void launch_split(const DecodeArgs& a, int path, int nw, int grid, hipStream_t st,
+                         hipEvent_t ev0, hipEvent_t ev1) {
   // 8-wave workgroups only for D <= 128 (the plan never picks them above)
   if constexpr (D <= 128) {
     if (nw == 8) {
-      if (path == 2) decode_mfma_kernel<D, 8, FUSED><<<grid, 512, 0, st>>>(a);
-      else decode_wave_kernel<D, 8, 4, FUSED><<<grid, 512, 0, st>>>(a);
+      if (path == 2) launch_timed(decode_mfma_kernel<D, 8, FUSED>, grid, 512, st, ev0, ev1, a);
+      else launch_timed(decode_wave_kernel<D, 8, 4, FUSED>, grid, 512, st, ev0, ev1, a);
       return;
     }
   }
-  if (path == 2) decode_mfma_kernel<D, 4, FUSED><<<grid, 256, 0, st>>>(a);
-  else decode_wave_kernel<D, 4, 4, FUSED><<<grid, 256, 0, st>>>(a);
+  if (path == 2) launch_timed(decode_mfma_kernel<D, 4, FUSED>, grid, 256, st, ev0, ev1, a);
+  else launch_timed(decode_wave_kernel<D, 4, 4, FUSED>, grid, 256, st, ev0, ev1, a);
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
-                                  hipStream_t st) {
+                                  hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   // the fused-merge code is compiled only into the kernels that use it
-  if (a.fused && !a.direct) launch_split<D, true>(a, path, nw, grid, st);
-  else launch_split<D, false>(a, path, nw, grid, st);
+  if (a.fused && !a.direct) launch_split<D, true>(a, path, nw, grid, st, ev0, ev1);
+  else launch_split<D, false>(a, path, nw, grid, st, ev0, ev1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.fused) return e;
   decode_combine_kernel<D><<<combine_grid, D < 64 ? 64 : D, 0, st>>>(a);
@@ -651,12 +664,12 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int gri
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
-                         hipStream_t st) {
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   switch (a.D) {
-    case 32: return launch_decode_d<32>(a, path, nw, grid, combine_grid, st);
-    case 64: return launch_decode_d<64>(a, path, nw, grid, combine_grid, st);
-    case 128: return launch_decode_d<128>(a, path, nw, grid, combine_grid, st);
-    case 256: return launch_decode_d<256>(a, path, nw, grid, combine_grid, st);
+    case 32: return launch_decode_d<32>(a, path, nw, grid, combine_grid, st, ev0, ev1);
+    case 64: return launch_decode_d<64>(a, path, nw, grid, combine_grid, st, ev0, ev1);
+    case 128: return launch_decode_d<128>(a, path, nw, grid, combine_grid, st, ev0, ev1);
+    case 256: return launch_decode_d<256>(a, path, nw, grid, combine_grid, st, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -47,10 +47,13 @@ struct PrefillArgs {
   int causal;
 };
 
+// ev0 / ev1 (may be null): measurement events stamped with the start / end
+// of the split (or direct) kernel's dispatch; the combine kernel is not timed.
 hipError_t launch_decode(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
-                         hipStream_t st);
+                         hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_clear_words(int32_t* words, int n, hipStream_t st);
-hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st,
+                          hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_padding_mask(const int32_t* cu, int B, int max_seqlen, uint8_t* mask,
                                hipStream_t st);
 hipError_t launch_clear_word(int32_t* word, hipStream_t st);

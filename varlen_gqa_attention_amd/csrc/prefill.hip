@@ -27,6 +27,8 @@
 // Workgroup order is XCD-aware: workgroup i runs on XCD i % 8, so the grid is
 // arranged such that each XCD walks whole (sequence, KV head) units, largest
 // query tiles first, keeping a unit's K/V in that XCD's L2 while its tiles run.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "launch.hpp"
 #include "plan.hpp"
@@ -349,9 +351,17 @@ __global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(Pref
   }
 }
 
+// With a measurement event pair the kernel is launched through
+// hipExtLaunchKernelGGL, which stamps the events with the dispatch's own start
+// and end.
 template <int D>
-static hipError_t launch_prefill_d(const PrefillArgs& a, int grid, hipStream_t st) {
-  prefill_kernel<D><<<grid, PrefillCfg<D>::THREADS, 0, st>>>(a);
+static hipError_t launch_prefill_d(const PrefillArgs& a, int grid, hipStream_t st, hipEvent_t ev0,
+                                   hipEvent_t ev1) {
+  if (ev0)
+    hipExtLaunchKernelGGL(prefill_kernel<D>, dim3(grid), dim3(PrefillCfg<D>::THREADS), 0, st, ev0,
+                          ev1, 0, a);
+  else
+    prefill_kernel<D><<<grid, PrefillCfg<D>::THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -360,12 +370,13 @@ static_assert(PrefillCfg<32>::ROWS == prefill_rows(32) && PrefillCfg<64>::ROWS =
                   PrefillCfg<256>::ROWS == prefill_rows(256),
               "plan and kernel disagree on the prefill tile");
 
-hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st) {
+hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st, hipEvent_t ev0,
+                          hipEvent_t ev1) {
   switch (D) {
-    case 32: return launch_prefill_d<32>(a, grid, st);
-    case 64: return launch_prefill_d<64>(a, grid, st);
-    case 128: return launch_prefill_d<128>(a, grid, st);
-    case 256: return launch_prefill_d<256>(a, grid, st);
+    case 32: return launch_prefill_d<32>(a, grid, st, ev0, ev1);
+    case 64: return launch_prefill_d<64>(a, grid, st, ev0, ev1);
+    case 128: return launch_prefill_d<128>(a, grid, st, ev0, ev1);
+    case 256: return launch_prefill_d<256>(a, grid, st, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }
