@@ -1,8 +1,8 @@
 """Comparison helpers for HIP-vs-oracle parity tests (no attention arithmetic).
 
 Tolerances: bf16 outputs within max |err| <= 1e-2 of the unrounded fp64
-oracle, widened to one bf16 ulp of the reference where that is larger (only
-possible for |O| >= 4, i.e. very short KV); fp32 LSE within 1e-3 relative
+oracle, widened to one bf16 ulp of the reference where that is larger (from
+|O| >= 2, where the ulp is 2^-6; only very short KV reaches such values); fp32 LSE within 1e-3 relative
 (|d| <= 1e-3 * max(1, |LSE|), since LSE can sit near 0); -inf must match
 exactly and NaN always fails.
 """

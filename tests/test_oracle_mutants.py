@@ -2,7 +2,7 @@
 
 Each mutant replaces one piece of oracle.attention for the duration of a test
 and re-runs the two independent references (scalar brute force and PyTorch
-SDPA). A mutant must disagree with at least one of them; otherwise the pins
+SDPA) against the direct and the split-KV forms. A mutant must disagree with at least one of them; otherwise the pins
 would not protect against that mistake.
 """
 import numpy as np
@@ -36,6 +36,19 @@ def _agrees_with_references(q, k, v, cu_q, cu_k, B, causal):
     for q0, Lq, o, ls, live in _sdpa_reference(q, k, v, cu_q, cu_k, B, causal):
         rows = np.arange(Lq)[live]
         if not np.allclose(out[q0 + rows], o[rows], rtol=1e-9, atol=1e-9):
+            return False
+    # the split-KV form (partials over 3-key ranges + LSE merge) against the
+    # same brute force
+    try:
+        out_s, lse_s, written_s = A.attend_varlen_split(q, k, v, cu_q, cu_k, B, causal, 3)
+    except (ValueError, IndexError):
+        return False
+    for (row, h), (o, ls) in ref.items():
+        if not written_s[row] or not np.allclose(out_s[row, h], o, rtol=1e-9, atol=1e-9):
+            return False
+        if np.isinf(ls) != np.isinf(lse_s[row, h]):
+            return False
+        if np.isfinite(ls) and abs(lse_s[row, h] - ls) > 1e-9:
             return False
     return True
 
@@ -71,6 +84,23 @@ def _lengths_from_start(cu, B, s_max=None):
 
 
 _ORIG_ROWS = A.attend_rows
+_ORIG_MERGE = A.merge_partials
+
+
+def _merge_weight_sign(o_parts, m_parts, l_parts):
+    m = np.asarray(m_parts, dtype=np.float64)
+    M = m.max(axis=0)
+    # weights exp(M - m_s) instead of exp(m_s - M)
+    return _ORIG_MERGE(o_parts, np.where(np.isfinite(m), 2 * np.where(np.isfinite(M), M, 0) - m, m),
+                       l_parts)
+
+
+def _merge_unweighted_l(o_parts, m_parts, l_parts):
+    O, LSE, M, L = _ORIG_MERGE(o_parts, m_parts, l_parts)
+    L2 = np.asarray(l_parts, dtype=np.float64).sum(axis=0)
+    live = np.isfinite(M)
+    O2 = np.where(live[..., None], O * (L / np.where(live, L2, 1.0))[..., None], 0.0)
+    return O2, LSE, M, L2
 
 MUTANTS = {
     "head map h % Hkv": ("kv_head_of", lambda h, Hq, Hkv: h % Hkv),
@@ -80,6 +110,8 @@ MUTANTS = {
     "output not normalised": ("attend_rows", _unnormalised),
     "LSE without the max": ("attend_rows", _lse_drops_max),
     "lengths from pack start": ("_lengths", _lengths_from_start),
+    "merge weights exp(M - m)": ("merge_partials", _merge_weight_sign),
+    "merge sums l unweighted": ("merge_partials", _merge_unweighted_l),
 }
 
 
