@@ -244,11 +244,23 @@ def cpu_baseline_long_decode(state, budget_s):
                        f"({dt:.2f} s each; K/V of bf16 values copied to host, untimed)")
 
 
+def visible_pairs(q_lens, kv_lens):
+    """(query, key) pairs a causal (bottom-right aligned) pass must compute:
+    query i of a sequence sees keys j <= i + Lk - Lq, clamped to [0, Lk)."""
+    total = 0
+    for lq, lk in zip(q_lens, kv_lens):
+        lq, lk = int(lq), int(lk)
+        shift = lk - lq
+        # rows i with i + shift + 1 in [0, lk]: count min(lk, max(0, i + shift + 1))
+        for i in range(lq):
+            total += min(lk, max(0, i + shift + 1))
+    return total
+
+
 def prefill_measure(args, reps=5):
     torch = _torch()
     import numpy as np
     import varlen_gqa_attention_amd as V
-    from oracle.attention import causal_pairs
     from varlen_gqa_attention_amd import inputs as I
     w = I.varlen_prefill(0)
     if getattr(args, "prefill_len", 0):
@@ -259,7 +271,7 @@ def prefill_measure(args, reps=5):
     plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], True)
     out = torch.empty_like(m["q"])
     lse = torch.empty(m["q"].shape[:2], device="cuda")
-    pairs = causal_pairs(m["cu_q_np"], m["cu_kv_np"], w["B"], True)
+    pairs = visible_pairs(w["q_lens"], w["kv_lens"])
     flop = 4 * w["Hq"] * w["D"] * pairs
     f = lambda: plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], out=out, lse=lse, B=w["B"])
     total, per = time_replays([f], reps, 2)
