@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define VATTN_ABI_VERSION 1
+#define VATTN_ABI_VERSION 2
 
 typedef void* vattn_stream_t; /* a hipStream_t */
 
@@ -96,6 +96,9 @@ typedef struct {
   int n_cu_override;        /* > 0: plan as if the device had this many CUs */
   int fuse_combine;         /* 1: last split workgroup of a unit merges (no 2nd launch); 0/2: combine kernel */
   int decode_waves;         /* 4 or 8 waves per decode workgroup; 0 = automatic */
+  int prefill_grid;         /* prefill: 0 = grid sized from B_max and s_max_q whose
+                               workgroups exit on dead tiles (default); 1 = device-built
+                               schedule of live tiles on a persistent grid */
 } vattn_plan_opts;
 
 typedef struct {
@@ -116,6 +119,7 @@ typedef struct {
   int q_tokens_per_tile; /* prefill: query tokens per workgroup (G heads folded) */
   int n_qtiles;        /* prefill: ceil(s_max_q / q_tokens_per_tile) */
   int threads;         /* threads per workgroup of the main kernel */
+  int prefill_persistent; /* prefill: 1 = schedule kernel + persistent grid of `grid` */
   long long scratch_bytes; /* device bytes owned by the plan */
 } vattn_plan_info;
 
@@ -155,10 +159,19 @@ vattn_status vattn_plan_query(vattn_plan_t p, vattn_plan_info* info);
  * B = 0 is a no-op). q_rows / kv_rows are the row capacities of q/out/lse and
  * k/v (tokens allocated); no row at or past them is read or written. The call
  * makes no host read of device data, no allocation and no synchronisation: it
- * enqueues one kernel (direct decode, fused split decode, prefill) or two
- * (split decode + combine) and returns. Pointers must be 16-byte aligned
- * (lse and cu: 4-byte). Rows of out/lse that belong to no sequence are not
- * written.
+ * enqueues one kernel (direct decode, fused split decode, prefill on the
+ * s_max grid) or two (split decode + combine; prefill schedule + persistent
+ * prefill) and returns. Pointers must be 16-byte aligned (lse and cu:
+ * 4-byte). Rows of out/lse that belong to no sequence are not written.
+ *
+ * Prefill work distribution (cudnn-frontend issue #552, How the other
+ * backends avoid this / Proposal to evaluate: the grid is sized at plan time
+ * and tiles read lengths on the device): by default the grid covers B_max x
+ * ceil(s_max_q / tile) tiles and workgroups on dead tiles exit after reading
+ * cu_seqlens; with prefill_grid = 1 a one-workgroup kernel reads
+ * cu_seqlens_q, lists the live (sequence, query tile) pairs in the plan's
+ * scratch, longest query tiles first, and a persistent grid of one
+ * workgroup per CU walks that list.
  */
 vattn_status vattn_execute(vattn_plan_t p, int B,
                            const void* q, const void* k, const void* v,

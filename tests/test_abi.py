@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (vattn_\w+)", out))
     assert set(declared_functions()) <= exported
-    assert L.vattn_abi_version() == 1
+    assert L.vattn_abi_version() == 2
 
 
 SWEEP = [(B, S, Hq, Hkv) for B in (1, 2, 33, 64, 300) for S in (1, 100, 4096, 32768)
@@ -57,10 +57,16 @@ def test_describe_equals_oracle_rule(B, S, Hq, Hkv, n_cu):
     want = choose_decode_split(B, S, units, n_cu, info["block_n"])
     for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
         assert info[key] == int(want[key]), key
+    # the default s_max grid follows the oracle's grid rule; the scheduled
+    # option (prefill_grid=1) is one workgroup per CU over a device-built list
     p = V.describe_plan(B, max(2, S), S, Hq, Hkv, 128, 1, n_cu_override=n_cu)
     g = choose_prefill_grid(B, max(2, S), Hkv, p["q_tokens_per_tile"])
-    assert p["n_qtiles"] == g["n_qtiles"]
+    assert p["n_qtiles"] == g["n_qtiles"] and p["prefill_persistent"] == 0
     assert p["grid"] == 8 * -(-(B * Hkv) // 8) * g["n_qtiles"]
+    d = V.describe_plan(B, max(2, S), S, Hq, Hkv, 128, 1, n_cu_override=n_cu, prefill_grid=1)
+    assert d["n_qtiles"] == g["n_qtiles"]
+    assert d["prefill_persistent"] == 1 and d["grid"] == n_cu
+    assert d["scratch_bytes"] == 512 + 4 * B * g["n_qtiles"]
 
 
 @pytest.mark.parametrize("force", [1, 2, 3, 7, 32, 100])

@@ -114,3 +114,29 @@ def test_kernel_event_hook():
     kern, whole = a.elapsed_time(b), t0.elapsed_time(t1)
     assert 0.0 < kern <= whole
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+
+@pytest.mark.parametrize("grid", [0, 1])
+def test_prefill_flags_a_sequence_with_no_live_tile(grid):
+    """A negative query length is clamped to 0 (no tile is ever scheduled for
+    that sequence) and still sets the error word; the other sequences are
+    computed as usual."""
+    import varlen_gqa_attention_amd as V
+    Hq, Hkv, D = 8, 2, 64
+    q = I.normal_bf16((60, Hq, D), 6, "cuda")
+    k = I.normal_bf16((60, Hkv, D), 7, "cuda")
+    v = I.normal_bf16((60, Hkv, D), 8, "cuda")
+    cu_q_np = np.array([0, 20, 50, 40], dtype=np.int32)        # sequence 2: query length -10
+    cu_kv_np = np.array([0, 20, 50, 60], dtype=np.int32)
+    plan = V.Plan(3, 64, 64, Hq, Hkv, D, True, prefill_grid=grid)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(60, Hq, device="cuda")
+    plan(q, k, v, torch.from_numpy(cu_q_np).cuda(), torch.from_numpy(cu_kv_np).cuda(), out=out,
+         lse=lse, B=3)
+    torch.cuda.synchronize()
+    assert plan.read_error() == V.ERRBIT_Q_LEN
+    ref_o, ref_l, wr = A.attend_varlen(I.bf16_to_f64(q), I.bf16_to_f64(k), I.bf16_to_f64(v),
+                                       cu_q_np, cu_kv_np, 3, True, s_max_q=64, s_max_kv=64)
+    assert wr.sum() == 50
+    assert_out_close(I.bf16_to_f64(out)[wr], ref_o[wr])
+    assert_lse_close(lse.cpu().numpy()[wr], ref_l[wr])

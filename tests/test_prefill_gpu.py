@@ -23,12 +23,13 @@ def _prefill_workload(name, Hq, Hkv, D, q_lens, kv_lens, causal=True, B_max=None
                 s_max_kv=s_max_kv or max(1, int(kv_lens.max())))
 
 
-def run_prefill(w, seed=0, picks=None):
+def run_prefill(w, seed=0, picks=None, **opts):
     import varlen_gqa_attention_amd as V
     print(f"[prefill] {w['name']} seed={seed} B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} D={w['D']} "
-          f"causal={w['causal']} q_lens={list(w['q_lens'])[:8]}", flush=True)
+          f"causal={w['causal']} q_lens={list(w['q_lens'])[:8]} opts={opts}", flush=True)
     m = I.materialise(w, seed, "cuda")
-    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], w["causal"])
+    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], w["causal"],
+                  **opts)
     out = torch.empty_like(m["q"]).view(torch.int16).fill_(SENT_OUT).view(torch.bfloat16)
     lse = torch.full(m["q"].shape[:2], SENT_LSE, dtype=torch.float32, device="cuda")
     plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], out=out, lse=lse, B=w["B"])
@@ -77,10 +78,14 @@ def test_odd_and_large_groups(G):
     run_prefill(_prefill_workload(f"G={G}", G, 1, 64, lens, lens, True), 3)
 
 
-def test_bottom_right_causal_with_unequal_lengths():
+GRIDS = [0, 1]  # s_max grid with dead-tile exit; device-built schedule on a persistent grid
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_bottom_right_causal_with_unequal_lengths(grid):
     # includes Lq > Lk (leading rows see no key) and Lq = 0
     w = _prefill_workload("Lq != Lk", 8, 2, 128, [5, 70, 0, 9, 40], [100, 30, 7, 0, 40], True)
-    run_prefill(w, 4)
+    run_prefill(w, 4, prefill_grid=grid)
 
 
 def test_noncausal_unequal_lengths():
@@ -88,16 +93,35 @@ def test_noncausal_unequal_lengths():
     run_prefill(w, 5)
 
 
-def test_tile_boundaries():
+@pytest.mark.parametrize("grid", GRIDS)
+def test_tile_boundaries(grid):
     lens = [31, 32, 33, 63, 64, 65, 95, 96, 97, 128]
-    run_prefill(_prefill_workload("boundaries", 32, 8, 128, lens, lens, True), 6)
+    run_prefill(_prefill_workload("boundaries", 32, 8, 128, lens, lens, True), 6, prefill_grid=grid)
 
 
-def test_unused_batch_slots_and_longer_cu_buffer():
+@pytest.mark.parametrize("grid", GRIDS)
+def test_unused_batch_slots_and_longer_cu_buffer(grid):
     w = _prefill_workload("B < B_max", 8, 2, 64, [17, 50], [17, 50], True, B_max=6, s_max_q=64,
                           s_max_kv=64)
     w["cu_capacity"], w["cu_tail"] = 9, [-1, 2**31 - 1, 0]
-    run_prefill(w, 7)
+    run_prefill(w, 7, prefill_grid=grid)
+
+
+def test_schedule_with_more_sequences_than_schedule_threads():
+    # 1500 sequences (the schedule kernel loops over them), many empty, lengths
+    # spanning zero to several query tiles
+    lens = np.random.default_rng([5, 1]).integers(0, 200, size=1500)
+    lens[::7] = 0
+    w = _prefill_workload("many sequences", 4, 1, 32, lens, lens, True, s_max_q=256, s_max_kv=256)
+    run_prefill(w, 9, prefill_grid=1)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_persistent_grid_smaller_than_work(D):
+    # few CUs' worth of workgroups walking many tiles each
+    lens = [300, 5, 257, 64, 1, 128]
+    run_prefill(_prefill_workload(f"n_cu=3 D={D}", 8, 2, D, lens, lens, True), 10,
+                n_cu_override=3, prefill_grid=1)
 
 
 def test_full_size_varlen_prefill_sampled():
@@ -112,16 +136,41 @@ def test_full_size_varlen_prefill_sampled():
     run_prefill(w, 0, picks=picks)
 
 
-def test_exact_grid_matches_oversubscribed_grid():
+def test_exact_grid_and_both_planned_grids_agree_bitwise():
+    import varlen_gqa_attention_amd as V
     w = _prefill_workload("exact grid", 32, 8, 128, [100, 1, 700, 64], [100, 1, 700, 64], True,
                           s_max_q=1024, s_max_kv=1024)
     plan, m, out, lse = run_prefill(w, 8)
+    assert plan.info["prefill_persistent"] == 0
     tq = plan.info["q_tokens_per_tile"]
     tiles = [(b << 16) | t for b, L in enumerate(w["q_lens"]) for t in range(-(-int(L) // tq))]
     tmap = torch.tensor(tiles[::-1], dtype=torch.int32, device="cuda")
     out2 = torch.empty_like(out)
     lse2 = torch.empty_like(lse)
     plan.execute_exact_grid(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], tmap, out2, lse2, w["B"])
+    plan1 = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], True,
+                   prefill_grid=1)
+    assert plan1.info["prefill_persistent"] == 1
+    out3 = torch.empty_like(out)
+    lse3 = torch.empty_like(lse)
+    plan1(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], out=out3, lse=lse3, B=w["B"])
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
-    assert torch.equal(lse, lse2)
+    for o, l in ((out2, lse2), (out3, lse3)):
+        assert torch.equal(out.view(torch.int16), o.view(torch.int16))
+        assert torch.equal(lse, l)
+
+
+def test_repeated_executes_reuse_the_schedule_bitwise():
+    # the schedule is rebuilt on every execute (new lengths, same plan)
+    import varlen_gqa_attention_amd as V
+    plan = V.Plan(4, 512, 512, 8, 2, 64, True, prefill_grid=1)
+    for step, lens in enumerate(([500, 3, 0, 77], [1, 512, 130, 9], [64, 64, 64, 64])):
+        w = _prefill_workload(f"step {step}", 8, 2, 64, lens, lens, True, s_max_q=512,
+                              s_max_kv=512)
+        m = I.materialise(w, 20 + step, "cuda")
+        out, lse = plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], B=4)
+        torch.cuda.synchronize()
+        q, k, v = (I.bf16_to_f64(m[n]) for n in ("q", "k", "v"))
+        ro, rl, wr = A.attend_varlen(q, k, v, m["cu_q_np"], m["cu_kv_np"], 4, True)
+        assert_out_close(I.bf16_to_f64(out)[wr], ro[wr], f"step {step}")
+        assert_lse_close(lse.cpu().numpy().astype(np.float64)[wr], rl[wr], f"step {step}")

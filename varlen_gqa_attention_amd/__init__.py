@@ -33,9 +33,9 @@ __all__ = ["Plan", "padding_mask", "describe_plan", "VattnError", "DECODE_AUTO",
 
 
 def _opts(target_blocks_per_cu=0, nsplit_cap=0, force_nsplit=0, force_decode_path=0,
-          n_cu_override=0, fuse_combine=0, decode_waves=0):
+          n_cu_override=0, fuse_combine=0, decode_waves=0, prefill_grid=0):
     return PlanOpts(target_blocks_per_cu, nsplit_cap, force_nsplit, force_decode_path,
-                    n_cu_override, fuse_combine, decode_waves)
+                    n_cu_override, fuse_combine, decode_waves, prefill_grid)
 
 
 def describe_plan(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, **opts):

@@ -33,14 +33,14 @@ EXPORTS = (
 class PlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "target_blocks_per_cu", "nsplit_cap", "force_nsplit", "force_decode_path",
-        "n_cu_override", "fuse_combine", "decode_waves")]
+        "n_cu_override", "fuse_combine", "decode_waves", "prefill_grid")]
 
 
 _INFO_INT_FIELDS = (
     "B_max", "s_max_q", "s_max_kv", "Hq", "Hkv", "D", "causal", "is_decode", "decode_path",
     "n_cu", "block_n", "n_tiles", "nsplit", "chunk_keys", "direct", "fused_combine",
     "head_blocks", "n_units", "grid", "combine_grid", "q_tokens_per_tile", "n_qtiles",
-    "threads")
+    "threads", "prefill_persistent")
 
 
 class PlanInfo(ctypes.Structure):

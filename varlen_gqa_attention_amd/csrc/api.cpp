@@ -21,6 +21,8 @@ struct vattn_plan_s {
   int32_t* counters;
   float2* part_ml;
   float* part_o;
+  int32_t* sched_count;  // prefill schedule: live-tile count, then the list
+  int32_t* sched_list;
   hipEvent_t ev_start, ev_stop;  // measurement hook (caller-owned), or null
 };
 
@@ -85,13 +87,17 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   if (!p) return VATTN_ERR_OOM;
   p->info = info;
   p->device = dev;
-  // layout: [0, 256) error word; merge counters; (m, l) pairs; O partials
+  // layout: [0, 256) error word; then for decode merge counters, (m, l)
+  // pairs and O partials; for a scheduled prefill [256, 512) the live-tile
+  // count and from 512 the list (B_max * n_qtiles entries)
   const uintptr_t n_cnt = info.direct ? 0 : (uintptr_t)info.n_units;
   const uintptr_t off_cnt = 256;
   uintptr_t off_ml = align_up(off_cnt + n_cnt * sizeof(int32_t), 256);
   uintptr_t n_part = info.direct ? 0 : (uintptr_t)B_max * Hq * info.nsplit;
   uintptr_t off_o = align_up(off_ml + n_part * sizeof(float2), 256);
   uintptr_t total = off_o + n_part * (uintptr_t)D * sizeof(float);
+  if (info.prefill_persistent)
+    total = 512 + (uintptr_t)B_max * info.n_qtiles * sizeof(int32_t);
   p->info.scratch_bytes = (long long)total;
   void* mem = nullptr;
   hipError_t e = hipMalloc(&mem, total);
@@ -105,6 +111,8 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   p->counters = n_cnt ? (int32_t*)(p->scratch + off_cnt) : nullptr;
   p->part_ml = n_part ? (float2*)(p->scratch + off_ml) : nullptr;
   p->part_o = n_part ? (float*)(p->scratch + off_o) : nullptr;
+  p->sched_count = info.prefill_persistent ? (int32_t*)(p->scratch + 256) : nullptr;
+  p->sched_list = info.prefill_persistent ? (int32_t*)(p->scratch + 512) : nullptr;
   // plan creation may synchronise (it is not on the hot path): zero the
   // error word once with a kernel, then wait for it.
   if (vattn::launch_clear_word(p->err, nullptr) != hipSuccess ||
@@ -199,6 +207,7 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.err = p->err;
     a.tile_map = tile_map;
     a.n_map = n_map;
+    a.sched_count = nullptr;
     a.B = B;
     a.B_max = in.B_max;
     a.Hq = in.Hq;
@@ -215,6 +224,13 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     const int64_t grid = tile_map ? (int64_t)n_map * in.Hkv : in.grid;
     if (grid == 0) return VATTN_OK;
     if (grid > INT32_MAX) return VATTN_ERR_UNSUPPORTED;
+    if (!tile_map && in.prefill_persistent) {
+      // the schedule kernel lists the live tiles; the persistent grid walks them
+      e = vattn::launch_prefill_schedule(a, p->sched_list, p->sched_count, st);
+      if (e != hipSuccess) return VATTN_ERR_HIP;
+      a.tile_map = p->sched_list;
+      a.sched_count = p->sched_count;
+    }
     e = vattn::launch_prefill(a, in.D, (int)grid, st, p->ev_start, p->ev_stop);
   }
   return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;

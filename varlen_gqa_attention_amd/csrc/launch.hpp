@@ -36,10 +36,15 @@ struct PrefillArgs {
   uint16_t* out;
   float* lse;
   int32_t* err;
-  const int32_t* tile_map;  // exact-grid comparator only (else null)
+  // Live-tile list, entries (b << 16) | q_tile: the caller's host-built map
+  // (exact-grid comparator, n_map entries, one workgroup per entry and KV
+  // head) or the device-built schedule (sched_count != null: the entry count
+  // is read on the device and a persistent grid strides over the list).
+  const int32_t* tile_map;
   int n_map;
+  const int32_t* sched_count;
   int B, B_max, Hq, Hkv, G;
-  int tq;        // query tokens per workgroup (rows = G * tq <= 128)
+  int tq;        // query tokens per workgroup (rows = G * tq)
   int n_qtiles;  // ceil(s_max_q / tq)
   int s_max_q, s_max_kv;
   int64_t q_rows, kv_rows;
@@ -54,6 +59,10 @@ hipError_t launch_decode(const DecodeArgs& a, int path, int nw, int grid, int co
 hipError_t launch_clear_words(int32_t* words, int n, hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st,
                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// Builds the live-tile list of a prefill pass into list / *count (one
+// workgroup); reads cu_seqlens_q (and cu_seqlens_kv, for the error word).
+hipError_t launch_prefill_schedule(const PrefillArgs& a, int32_t* list, int32_t* count,
+                                   hipStream_t st);
 hipError_t launch_padding_mask(const int32_t* cu, int B, int max_seqlen, uint8_t* mask,
                                hipStream_t st);
 hipError_t launch_clear_word(int32_t* word, hipStream_t st);

@@ -104,13 +104,26 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     const int64_t grid = 8 * ((units + 7) / 8) * (int64_t)in.n_qtiles;
     if (grid > (1LL << 31) - 1) return VATTN_ERR_UNSUPPORTED;
     in.n_units = (int)units;
-    in.grid = (int)grid;
     in.threads = prefill_threads(D);
     in.block_n = 64;
     in.n_tiles = cdiv(s_max_kv, 64);
     in.nsplit = 1;
     in.direct = 1;
-    in.scratch_bytes = 256;
+    // Default: the grid covers B_max x n_qtiles tiles and workgroups on dead
+    // tiles exit (measured as fast as the alternatives on this chip: a dead
+    // workgroup costs well under a microsecond, and the unit-major order keeps
+    // a unit's K/V in its XCD's L2). Option 1: a schedule kernel lists the
+    // live tiles on the device, longest first, and a persistent grid (one
+    // workgroup per CU) walks the list; not available when the schedule's
+    // per-level table would not fit in LDS.
+    in.prefill_persistent = (o.prefill_grid == 1 && in.n_qtiles <= kSchedMaxQtiles) ? 1 : 0;
+    if (in.prefill_persistent) {
+      in.grid = n_cu;
+      in.scratch_bytes = 512 + (int64_t)B_max * in.n_qtiles * 4;
+    } else {
+      in.grid = (int)grid;
+      in.scratch_bytes = 256;
+    }
   }
   *info = in;
   return VATTN_OK;

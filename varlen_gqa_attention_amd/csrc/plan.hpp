@@ -14,6 +14,8 @@ constexpr int kWaveMaxG = 4;          // auto: G <= this uses the wave path
 // of 32 rows; threads per prefill workgroup
 constexpr int prefill_rows(int D) { return D <= 128 ? 256 : 128; }
 constexpr int prefill_threads(int D) { return D <= 128 ? 512 : 256; }
+// largest query-tile count per sequence the on-device prefill schedule handles
+constexpr int kSchedMaxQtiles = 8192;
 
 // Fills *info (sizes only; no allocation). n_cu must be > 0.
 vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv, int D,

@@ -62,32 +62,15 @@ struct PrefillCfg {
   static constexpr int THREADS = NW * 64;
 };
 
+// One query tile (sequence b, KV head hk, query tile qt) of the pass; the
+// whole workgroup calls it with the same arguments (every exit is uniform).
 template <int D>
-__global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds, int b, int hk,
+                                             int qt) {
   using C = PrefillCfg<D>;
   constexpr int NW = C::NW, RB = C::RB, BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK;
   constexpr int NSTAGE = C::NSTAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * 2 * C::TILE_BYTES];
-
-  // ---- which (sequence, kv head, query tile)
-  int b, hk, qt;
-  if (a.tile_map) {
-    const int e = blockIdx.x / a.Hkv;
-    hk = blockIdx.x % a.Hkv;
-    if (e >= a.n_map) return;
-    const int entry = a.tile_map[e];
-    b = entry >> 16;
-    qt = entry & 0xffff;
-    if (b < 0 || qt >= a.n_qtiles) return;
-  } else {
-    const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
-    const int u = x + 8 * (p / a.n_qtiles);
-    qt = a.n_qtiles - 1 - p % a.n_qtiles;
-    if (u >= a.B_max * a.Hkv) return;
-    b = u / a.Hkv;
-    hk = u % a.Hkv;
-  }
-  if (b >= a.B) return;
+  if (b < 0 || b >= a.B || qt >= a.n_qtiles) return;
   const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
   const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
   if (qt == 0 && hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
@@ -351,6 +334,106 @@ __global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(Pref
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(PrefillArgs a) {
+  using C = PrefillCfg<D>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * 2 * C::TILE_BYTES];
+  if (a.sched_count) {
+    // persistent: stride over (list entry, KV head) pairs; the list is
+    // ordered longest query tiles first, so each round of the stride holds
+    // tiles of similar cost
+    const int total = *a.sched_count * a.Hkv;
+    for (int f = blockIdx.x; f < total; f += gridDim.x) {
+      const int entry = a.tile_map[f / a.Hkv];
+      prefill_tile<D>(a, lds, entry >> 16, f % a.Hkv, entry & 0xffff);
+      __syncthreads();  // the next tile reuses the LDS ring
+    }
+  } else if (a.tile_map) {
+    const int e = blockIdx.x / a.Hkv;
+    if (e >= a.n_map) return;
+    const int entry = a.tile_map[e];
+    prefill_tile<D>(a, lds, entry >> 16, blockIdx.x % a.Hkv, entry & 0xffff);
+  } else {
+    // grid from B_max and s_max_q: workgroup i runs on XCD i % 8, and each
+    // XCD walks whole (sequence, KV head) units, longest query tiles first
+    const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
+    const int u = x + 8 * (p / a.n_qtiles);
+    if (u >= a.B_max * a.Hkv) return;
+    prefill_tile<D>(a, lds, u / a.Hkv, u % a.Hkv, a.n_qtiles - 1 - p % a.n_qtiles);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Device-built schedule of live query tiles (one workgroup). With n(b) =
+// ceil(Lq_b / tq) live tiles for sequence b, the list holds level qt =
+// n_qtiles - 1 down to 0, and within a level the sequences with n(b) > qt in
+// order of decreasing n(b) (a counting sort): entry position =
+// off(qt) + rank(b), where rank(b) = #{b' : n(b') > n(b)} + (place among
+// equal n), and off(qt) = sum over levels above qt of their sizes.
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+
+// out[i] = sum of v[j] for j > i (exclusive suffix sum), i < n, in place.
+__device__ void block_suffix_sum(int* v, int n, int* part) {
+  const int t = threadIdx.x;
+  const int per = (n + kSchedThreads - 1) / kSchedThreads;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += v[i];
+  part[t] = sum;
+  __syncthreads();
+  // suffix scan of the per-thread sums (Hillis-Steele)
+  for (int d = 1; d < kSchedThreads; d <<= 1) {
+    const int add = (t + d < kSchedThreads) ? part[t + d] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int acc = (t + 1 < kSchedThreads) ? part[t + 1] : 0;  // sum of chunks after this one
+  for (int i = hi - 1; i >= lo; --i) {
+    const int x = v[i];
+    v[i] = acc;
+    acc += x;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(PrefillArgs a,
+                                                                        int32_t* list,
+                                                                        int32_t* count) {
+  __shared__ int hist[kSchedMaxQtiles + 1];  // sequences per live-tile count
+  __shared__ int lvl[kSchedMaxQtiles + 1];   // per level: its offset in the list
+  __shared__ int part[kSchedThreads];
+  const int NQ = a.n_qtiles, t = threadIdx.x;
+  for (int i = t; i <= NQ; i += kSchedThreads) hist[i] = 0;
+  __syncthreads();
+  int flags = 0;
+  for (int b = t; b < a.B; b += kSchedThreads) {
+    const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
+    const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
+    flags |= sq.flags | sk.flags;
+    atomicAdd(&hist[(sq.len + a.tq - 1) / a.tq], 1);
+  }
+  report(a.err, flags);
+  __syncthreads();
+  // hist[n] -> #{b : n(b) > n} (the first rank of count n, and the size of
+  // level n), then the level sizes -> level offsets
+  block_suffix_sum(hist, NQ + 1, part);
+  for (int i = t; i < NQ; i += kSchedThreads) lvl[i] = hist[i];
+  __syncthreads();
+  block_suffix_sum(lvl, NQ, part);
+  if (t == 0) *count = NQ > 0 ? lvl[0] + hist[0] : 0;
+  // ranks: the rank counter of count n starts at hist[n] (sequences with
+  // more live tiles come first) and is bumped per sequence
+  for (int b = t; b < a.B; b += kSchedThreads) {
+    const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
+    const int n = (sq.len + a.tq - 1) / a.tq;
+    if (n == 0) continue;
+    const int r = atomicAdd(&hist[n], 1);
+    for (int qt = 0; qt < n; ++qt) list[lvl[qt] + r] = (b << 16) | qt;
+  }
+}
+
 // With a measurement event pair the kernel is launched through
 // hipExtLaunchKernelGGL, which stamps the events with the dispatch's own start
 // and end.
@@ -369,6 +452,13 @@ static_assert(PrefillCfg<32>::ROWS == prefill_rows(32) && PrefillCfg<64>::ROWS =
                   PrefillCfg<128>::ROWS == prefill_rows(128) &&
                   PrefillCfg<256>::ROWS == prefill_rows(256),
               "plan and kernel disagree on the prefill tile");
+
+hipError_t launch_prefill_schedule(const PrefillArgs& a, int32_t* list, int32_t* count,
+                                   hipStream_t st) {
+  if (a.n_qtiles > kSchedMaxQtiles) return hipErrorInvalidValue;
+  prefill_schedule_kernel<<<1, kSchedThreads, 0, st>>>(a, list, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int D, int grid, hipStream_t st, hipEvent_t ev0,
                           hipEvent_t ev1) {

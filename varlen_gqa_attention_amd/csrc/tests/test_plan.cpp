@@ -33,13 +33,25 @@ int main() {
   // batch * kv heads fills the device: direct write
   CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0 && in.decode_path == VATTN_DECODE_WAVE);
-  // prefill grid from B_max and s_max_q, G heads folded into 256 rows (D <= 128)
+  // prefill: G heads folded into 256 rows (D <= 128); default grid from
+  // B_max and s_max_q
   CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 128, 1, nullptr, 256, &in) == VATTN_OK);
-  CHECK(!in.is_decode && in.q_tokens_per_tile == 64 && in.n_qtiles == 64 && in.grid == 8192);
-  CHECK(in.threads == 512);
+  CHECK(!in.is_decode && in.q_tokens_per_tile == 64 && in.n_qtiles == 64);
+  CHECK(in.prefill_persistent == 0 && in.grid == 8192 && in.threads == 512);
   // D = 256: 128 rows, 4 waves
   CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 256, 1, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.q_tokens_per_tile == 32 && in.n_qtiles == 128 && in.grid == 16384 && in.threads == 256);
+  {
+    // device-built schedule: persistent grid of one workgroup per CU over a
+    // list of B_max * n_qtiles slots
+    vattn_plan_opts g = {};
+    g.prefill_grid = 1;
+    CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 128, 1, &g, 256, &in) == VATTN_OK);
+    CHECK(in.prefill_persistent == 1 && in.grid == 256 && in.scratch_bytes == 512 + 16 * 64 * 4);
+    // more query tiles than the schedule handles: stays on the s_max grid
+    CHECK(vattn::plan_compute(1, 8193 * 64, 64, 4, 1, 128, 1, &g, 256, &in) == VATTN_OK);
+    CHECK(in.n_qtiles == 8193 && in.prefill_persistent == 0);
+  }
   // validation
   CHECK(vattn::plan_compute(1, 1, 64, 6, 4, 64, 0, nullptr, 256, &in) == VATTN_ERR_INVALID_ARG);
   CHECK(vattn::plan_compute(1, 1, 64, 8, 2, 80, 0, nullptr, 256, &in) == VATTN_ERR_UNSUPPORTED);
