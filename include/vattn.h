@@ -210,6 +210,20 @@ vattn_status vattn_padding_mask(const int32_t* cu_seqlens, int B, int max_seqlen
                                 uint8_t* mask, vattn_stream_t stream);
 
 /*
+ * Cross-attention padding masks (TransformerEngine PR #24, Equivalence: the
+ * query-side and the key-side mask of one batch), built in one launch:
+ * mask_q[b * max_seqlen_q + p] = (p >= cu_q[b+1] - cu_q[b]) for p <
+ * max_seqlen_q, and mask_kv likewise from cu_kv and max_seqlen_kv. Layout,
+ * wraparound, invalid-length and trailing-entry rules as vattn_padding_mask.
+ * Either side may have max_seqlen 0 (its pointer may then be NULL). Caller-
+ * owned buffers; returns VATTN_ERR_INVALID_ARG for negative sizes or missing
+ * pointers, nothing is enqueued then.
+ */
+vattn_status vattn_cross_padding_mask(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                      int B, int max_seqlen_q, int max_seqlen_kv,
+                                      uint8_t* mask_q, uint8_t* mask_kv, vattn_stream_t stream);
+
+/*
  * Device address of the plan's int32 error word (VATTN_ERRBIT_*). The caller
  * reads it after its own synchronisation; the library never does.
  */

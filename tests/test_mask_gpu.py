@@ -71,3 +71,42 @@ def test_invalid_lengths_follow_the_formula():
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), M.padding_mask(cu, B, ms))
     assert out.shape == (B, 1, 1, ms) and out.dtype == torch.bool
+
+
+def test_exhaustive_cross_attention_cases():
+    """Every combination of query and key lengths for max_seqlen_q, max_seqlen_kv
+    in 1..5 and batch 1..3 (the page's 202100 cases). The cases of one
+    (max_q, max_kv, B) shape are laid end to end as one batch (a mask row
+    depends only on its own sequence's length), one launch per shape."""
+    import varlen_gqa_attention_amd as V
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "te24_mask_equivalence.json")))["cross_attention"]
+    n_cases = 0
+    for mq in range(g["max_seqlen_q"][0], g["max_seqlen_q"][1] + 1):
+        for mk in range(g["max_seqlen_kv"][0], g["max_seqlen_kv"][1] + 1):
+            for B in range(g["batch_size"][0], g["batch_size"][1] + 1):
+                pairs = list(itertools.product(range(mq + 1), range(mk + 1)))
+                combos = list(itertools.product(pairs, repeat=B))
+                n_cases += len(combos)
+                lq = np.array([p[0] for c in combos for p in c], dtype=np.int64)
+                lk = np.array([p[1] for c in combos for p in c], dtype=np.int64)
+                cu_q = I.cu_from_lengths(lq)
+                cu_k = I.cu_from_lengths(lk)
+                n = lq.size
+                got_q, got_k = V.cross_padding_masks(torch.from_numpy(cu_q).cuda(),
+                                                     torch.from_numpy(cu_k).cuda(), n, mq, mk)
+                ref_q, ref_k = M.cross_padding_masks(cu_q, cu_k, n, mq, mk)
+                assert np.array_equal(got_q.cpu().numpy(), ref_q), (mq, mk, B)
+                assert np.array_equal(got_k.cpu().numpy(), ref_k), (mq, mk, B)
+    assert n_cases == g["cases"]
+
+
+def test_cross_masks_with_longer_buffers_and_invalid_lengths():
+    import varlen_gqa_attention_amd as V
+    cu_q = np.array([0, 3, 1, 9, -7, 100], dtype=np.int32)     # lengths 3, -2, 8; tail ignored
+    cu_k = np.array([5, 5, 2**31 - 1, 0, 44, 3], dtype=np.int32)
+    got_q, got_k = V.cross_padding_masks(torch.from_numpy(cu_q).cuda(),
+                                         torch.from_numpy(cu_k).cuda(), 3, 6, 4)
+    ref_q, ref_k = M.cross_padding_masks(cu_q, cu_k, 3, 6, 4)
+    assert np.array_equal(got_q.cpu().numpy(), ref_q)
+    assert np.array_equal(got_k.cpu().numpy(), ref_k)

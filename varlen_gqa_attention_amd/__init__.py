@@ -28,7 +28,7 @@ class _LazyLib:
 
 _LIB = _LazyLib()
 
-__all__ = ["Plan", "padding_mask", "describe_plan", "VattnError", "DECODE_AUTO",
+__all__ = ["Plan", "padding_mask", "cross_padding_masks", "describe_plan", "VattnError", "DECODE_AUTO",
            "DECODE_WAVE", "DECODE_MFMA", "ERRBIT_Q_LEN", "ERRBIT_KV_LEN", "ERRBIT_ROWS"]
 
 
@@ -165,6 +165,31 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def cross_padding_masks(cu_seqlens_q, cu_seqlens_kv, B, max_seqlen_q, max_seqlen_kv,
+                        out_q=None, out_kv=None, stream=None):
+    """(bool [B, 1, 1, max_seqlen_q], bool [B, 1, 1, max_seqlen_kv]): the
+    query-side and key-side padding masks of a cross-attention batch."""
+    import torch
+    for cu in (cu_seqlens_q, cu_seqlens_kv):
+        if cu.dtype != torch.int32 or not cu.is_cuda or not cu.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 device tensors")
+        if cu.numel() < B + 1:
+            raise ValueError("cu_seqlens needs at least B + 1 entries")
+    dev = cu_seqlens_q.device
+    if out_q is None:
+        out_q = torch.empty((B, 1, 1, max_seqlen_q), dtype=torch.bool, device=dev)
+    if out_kv is None:
+        out_kv = torch.empty((B, 1, 1, max_seqlen_kv), dtype=torch.bool, device=dev)
+    for o, n in ((out_q, max_seqlen_q), (out_kv, max_seqlen_kv)):
+        if o.dtype != torch.bool or not o.is_contiguous() or o.numel() != B * n:
+            raise ValueError("outputs must be contiguous bool tensors of B * max_seqlen elements")
+    _lib.check(_LIB.vattn_cross_padding_mask(_ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), B,
+                                             max_seqlen_q, max_seqlen_kv, _ptr(out_q),
+                                             _ptr(out_kv), _stream_of(cu_seqlens_q, stream)),
+               "vattn_cross_padding_mask")
+    return out_q, out_kv
 
 
 def padding_mask(cu_seqlens, B, max_seqlen, out=None, stream=None):

@@ -24,7 +24,8 @@ ERRBIT_Q_LEN, ERRBIT_KV_LEN, ERRBIT_ROWS = 0x1, 0x2, 0x4
 EXPORTS = (
     "vattn_status_string", "vattn_abi_version", "vattn_plan", "vattn_plan_ex",
     "vattn_plan_describe", "vattn_plan_query", "vattn_execute",
-    "vattn_execute_exact_grid", "vattn_padding_mask", "vattn_plan_error_word",
+    "vattn_execute_exact_grid", "vattn_padding_mask", "vattn_cross_padding_mask",
+    "vattn_plan_error_word",
     "vattn_plan_read_error", "vattn_plan_clear_error", "vattn_plan_set_kernel_events",
     "vattn_plan_destroy",
 )
@@ -92,6 +93,8 @@ def load():
                                            vp, c_int, vp]
     L.vattn_padding_mask.restype = c_int
     L.vattn_padding_mask.argtypes = [vp, c_int, c_int, vp, vp]
+    L.vattn_cross_padding_mask.restype = c_int
+    L.vattn_cross_padding_mask.argtypes = [vp, vp, c_int, c_int, c_int, vp, vp, vp]
     L.vattn_plan_error_word.restype = vp
     L.vattn_plan_error_word.argtypes = [vp]
     L.vattn_plan_read_error.restype = c_int

@@ -274,6 +274,21 @@ vattn_status vattn_plan_set_kernel_events(vattn_plan_t p, void* start, void* sto
   return VATTN_OK;
 }
 
+vattn_status vattn_cross_padding_mask(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                      int B, int max_seqlen_q, int max_seqlen_kv,
+                                      uint8_t* mask_q, uint8_t* mask_kv, vattn_stream_t stream) {
+  if (B < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0) return VATTN_ERR_INVALID_ARG;
+  if (B == 0 || (max_seqlen_q == 0 && max_seqlen_kv == 0)) return VATTN_OK;
+  if (!cu_seqlens_q || !cu_seqlens_kv || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+    return VATTN_ERR_INVALID_ARG;
+  if ((max_seqlen_q > 0 && !mask_q) || (max_seqlen_kv > 0 && !mask_kv))
+    return VATTN_ERR_INVALID_ARG;
+  hipError_t e = vattn::launch_cross_padding_mask(cu_seqlens_q, cu_seqlens_kv, B, max_seqlen_q,
+                                                  max_seqlen_kv, mask_q, mask_kv,
+                                                  (hipStream_t)stream);
+  return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
+}
+
 const int32_t* vattn_plan_error_word(vattn_plan_t p) { return p ? p->err : nullptr; }
 
 vattn_status vattn_plan_read_error(vattn_plan_t p, int32_t* value) {

@@ -65,6 +65,9 @@ hipError_t launch_prefill_schedule(const PrefillArgs& a, int32_t* list, int32_t*
                                    hipStream_t st);
 hipError_t launch_padding_mask(const int32_t* cu, int B, int max_seqlen, uint8_t* mask,
                                hipStream_t st);
+hipError_t launch_cross_padding_mask(const int32_t* cu_q, const int32_t* cu_kv, int B,
+                                     int max_q, int max_kv, uint8_t* mask_q, uint8_t* mask_kv,
+                                     hipStream_t st);
 hipError_t launch_clear_word(int32_t* word, hipStream_t st);
 
 }  // namespace vattn

@@ -14,10 +14,9 @@ __device__ __forceinline__ int len_i32(const int32_t* cu, int64_t b) {
   return (int)((uint32_t)cu[b + 1] - (uint32_t)cu[b]);  // int32 wraparound
 }
 
-__global__ __launch_bounds__(256) void padding_mask_kernel(const int32_t* __restrict__ cu,
-                                                           int max_seqlen, int64_t total,
-                                                           uint8_t* __restrict__ mask,
-                                                           int vec) {
+// Grid-stride body shared by the single and the cross-attention kernels.
+__device__ __forceinline__ void build_mask(const int32_t* __restrict__ cu, int max_seqlen,
+                                           int64_t total, uint8_t* __restrict__ mask, int vec) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x * 16;
   for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; base < total;
        base += stride) {
@@ -42,6 +41,30 @@ __global__ __launch_bounds__(256) void padding_mask_kernel(const int32_t* __rest
   }
 }
 
+__global__ __launch_bounds__(256) void padding_mask_kernel(const int32_t* __restrict__ cu,
+                                                           int max_seqlen, int64_t total,
+                                                           uint8_t* __restrict__ mask,
+                                                           int vec) {
+  build_mask(cu, max_seqlen, total, mask, vec);
+}
+
+// Cross attention (TransformerEngine PR #24, Equivalence: query-side and
+// key-side masks of one batch): blockIdx.y = 0 builds the query mask, 1 the
+// key mask, in one launch.
+struct MaskSide {
+  const int32_t* cu;
+  uint8_t* mask;
+  int64_t total;
+  int max_seqlen;
+  int vec;
+};
+
+__global__ __launch_bounds__(256) void cross_padding_mask_kernel(MaskSide q, MaskSide kv) {
+  const MaskSide& m = blockIdx.y == 0 ? q : kv;
+  if (m.total == 0) return;
+  build_mask(m.cu, m.max_seqlen, m.total, m.mask, m.vec);
+}
+
 __global__ void clear_word_kernel(int32_t* w) {
   if (threadIdx.x == 0) *w = 0;
 }
@@ -55,6 +78,23 @@ hipError_t launch_padding_mask(const int32_t* cu, int B, int max_seqlen, uint8_t
   if (blocks > 65536) blocks = 65536;
   const int vec = ((uintptr_t)mask & 15) == 0;
   padding_mask_kernel<<<(unsigned)blocks, 256, 0, st>>>(cu, max_seqlen, total, mask, vec);
+  return hipGetLastError();
+}
+
+static int64_t mask_blocks(int64_t total) {
+  const int64_t chunks = (total + 15) / 16;
+  const int64_t blocks = (chunks + 255) / 256;
+  return blocks > 65536 ? 65536 : blocks;
+}
+
+hipError_t launch_cross_padding_mask(const int32_t* cu_q, const int32_t* cu_kv, int B,
+                                     int max_q, int max_kv, uint8_t* mask_q, uint8_t* mask_kv,
+                                     hipStream_t st) {
+  MaskSide q{cu_q, mask_q, (int64_t)B * max_q, max_q, ((uintptr_t)mask_q & 15) == 0};
+  MaskSide kv{cu_kv, mask_kv, (int64_t)B * max_kv, max_kv, ((uintptr_t)mask_kv & 15) == 0};
+  const int64_t blocks = mask_blocks(q.total > kv.total ? q.total : kv.total);
+  if (blocks == 0) return hipSuccess;
+  cross_padding_mask_kernel<<<dim3((unsigned)blocks, 2), 256, 0, st>>>(q, kv);
   return hipGetLastError();
 }
 
