@@ -181,6 +181,26 @@ vattn_status vattn_execute(vattn_plan_t p, int B,
                            vattn_stream_t stream);
 
 /*
+ * vattn_execute on token-row-strided views (cudnn-frontend issue #552,
+ * Related / Proposal: binding the caller's ragged layout directly, e.g. q, k
+ * and v as slices of one fused QKV buffer). Row t of q starts at element
+ * t * q_row_stride of q (likewise k, v and out); within a row the heads are
+ * contiguous with stride D. A stride of 0 means packed (H * D). Each stride
+ * must be >= H * D of its tensor and a multiple of 8 elements (16 bytes);
+ * otherwise VATTN_ERR_INVALID_ARG and nothing is enqueued. q_rows / kv_rows
+ * count rows: the caller's buffers must hold (rows - 1) * stride + H * D
+ * elements. lse stays packed [T_q, Hq]. Same results as vattn_execute on
+ * packed copies (bit-identical).
+ */
+vattn_status vattn_execute_strided(vattn_plan_t p, int B,
+                                   const void* q, int64_t q_row_stride,
+                                   const void* k, int64_t k_row_stride,
+                                   const void* v, int64_t v_row_stride,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                   void* out, int64_t out_row_stride, float* lse,
+                                   int64_t q_rows, int64_t kv_rows, vattn_stream_t stream);
+
+/*
  * Prefill comparator that the grid-sizing question asks to be measured
  * (cudnn-frontend issue #552, Proposal to evaluate: exact grid versus
  * oversubscription with early exit). tile_map holds n_tiles int32 entries,

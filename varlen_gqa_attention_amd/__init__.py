@@ -72,7 +72,9 @@ class Plan:
         self.B_max, self.Hq, self.Hkv, self.D = B_max, Hq, Hkv, D
 
     # -- tensors -----------------------------------------------------------
-    def _check(self, q, k, v, cu_q, cu_kv, out, lse):
+    def _check(self, q, k, v, cu_q, cu_kv, out, lse, row_strided=False):
+        """Metadata checks. With row_strided, q / k / v / out may be views whose
+        token dimension has any stride (heads and head dims contiguous)."""
         import torch
         for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
                             ("v", v, torch.bfloat16), ("out", out, torch.bfloat16),
@@ -82,7 +84,10 @@ class Plan:
                 raise TypeError(f"{name} must be {dt}, got {t.dtype}")
             if not t.is_cuda:
                 raise ValueError(f"{name} must be a device tensor")
-            if not t.is_contiguous():
+            if row_strided and name in ("q", "k", "v", "out") and t.dim() == 3:
+                if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+                    raise ValueError(f"{name}: heads and head dims must be contiguous")
+            elif not t.is_contiguous():
                 raise ValueError(f"{name} must be contiguous")
         if q.dim() != 3 or q.shape[1:] != (self.Hq, self.D):
             raise ValueError(f"q must be [T_q, {self.Hq}, {self.D}], got {tuple(q.shape)}")
@@ -106,10 +111,18 @@ class Plan:
             B = cu_seqlens_q.numel() - 1
         if cu_seqlens_q.numel() < B + 1 or cu_seqlens_kv.numel() < B + 1:
             raise ValueError("cu_seqlens buffers need at least B + 1 entries")
-        self._check(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, lse)
-        _lib.check(_LIB.vattn_execute(self._h, B, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
-                                      _ptr(cu_seqlens_kv), _ptr(out), _ptr(lse), q.shape[0],
-                                      k.shape[0], _stream_of(q, stream)), "vattn_execute")
+        self._check(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, lse, row_strided=True)
+        if all(t.is_contiguous() for t in (q, k, v, out)):
+            _lib.check(_LIB.vattn_execute(self._h, B, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out),
+                                          _ptr(lse), q.shape[0], k.shape[0],
+                                          _stream_of(q, stream)), "vattn_execute")
+        else:
+            # token-row-strided views (e.g. slices of a fused QKV buffer)
+            _lib.check(_LIB.vattn_execute_strided(
+                self._h, B, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out), out.stride(0), _ptr(lse),
+                q.shape[0], k.shape[0], _stream_of(q, stream)), "vattn_execute_strided")
         return out, lse
 
     def execute_exact_grid(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, tile_map, out, lse, B,

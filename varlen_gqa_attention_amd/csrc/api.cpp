@@ -152,10 +152,20 @@ static vattn_status check_exec(vattn_plan_t p, int B, const void* q, const void*
   return VATTN_OK;
 }
 
+// Row (token) strides in elements of q, k, v and out.
+struct Strides {
+  int64_t q, k, v, o;
+};
+
+static Strides packed_strides(const vattn_plan_info& in) {
+  return Strides{(int64_t)in.Hq * in.D, (int64_t)in.Hkv * in.D, (int64_t)in.Hkv * in.D,
+                 (int64_t)in.Hq * in.D};
+}
+
 static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
                         const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
                         int64_t q_rows, int64_t kv_rows, const int32_t* tile_map, int n_map,
-                        vattn_stream_t stream) {
+                        const Strides& rs, vattn_stream_t stream) {
   const vattn_plan_info& in = p->info;
   const float c = (float)(1.0 / std::sqrt((double)in.D) * 1.4426950408889634);
   hipStream_t st = (hipStream_t)stream;
@@ -190,6 +200,10 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.s_max_kv = in.s_max_kv;
     a.q_rows = q_rows;
     a.kv_rows = kv_rows;
+    a.q_rs = rs.q;
+    a.k_rs = rs.k;
+    a.v_rs = rs.v;
+    a.o_rs = rs.o;
     a.c = c;
     a.direct = in.direct;
     a.fused = in.fused_combine;
@@ -219,6 +233,10 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.s_max_kv = in.s_max_kv;
     a.q_rows = q_rows;
     a.kv_rows = kv_rows;
+    a.q_rs = rs.q;
+    a.k_rs = rs.k;
+    a.v_rs = rs.v;
+    a.o_rs = rs.o;
     a.c = c;
     a.causal = in.causal;
     const int64_t grid = tile_map ? (int64_t)n_map * in.Hkv : in.grid;
@@ -241,7 +259,30 @@ vattn_status vattn_execute(vattn_plan_t p, int B, const void* q, const void* k, 
                            int64_t q_rows, int64_t kv_rows, vattn_stream_t stream) {
   vattn_status st = check_exec(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows);
   if (st != VATTN_OK || B == 0) return st;
-  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, nullptr, 0, stream);
+  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, nullptr, 0,
+             packed_strides(p->info), stream);
+}
+
+vattn_status vattn_execute_strided(vattn_plan_t p, int B, const void* q, int64_t q_row_stride,
+                                   const void* k, int64_t k_row_stride, const void* v,
+                                   int64_t v_row_stride, const int32_t* cu_q,
+                                   const int32_t* cu_kv, void* out, int64_t out_row_stride,
+                                   float* lse, int64_t q_rows, int64_t kv_rows,
+                                   vattn_stream_t stream) {
+  vattn_status st = check_exec(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows);
+  if (st != VATTN_OK) return st;
+  const vattn_plan_info& in = p->info;
+  const Strides packed = packed_strides(in);
+  const Strides rs{q_row_stride ? q_row_stride : packed.q, k_row_stride ? k_row_stride : packed.k,
+                   v_row_stride ? v_row_stride : packed.v,
+                   out_row_stride ? out_row_stride : packed.o};
+  // every row holds its heads contiguously (head stride D); rows keep the
+  // 16-byte alignment of the base pointers and do not overlap
+  if (rs.q < packed.q || rs.k < packed.k || rs.v < packed.v || rs.o < packed.o)
+    return VATTN_ERR_INVALID_ARG;
+  if ((rs.q | rs.k | rs.v | rs.o) & 7) return VATTN_ERR_INVALID_ARG;
+  if (B == 0) return VATTN_OK;
+  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, nullptr, 0, rs, stream);
 }
 
 vattn_status vattn_execute_exact_grid(vattn_plan_t p, int B, const void* q, const void* k,
@@ -255,7 +296,8 @@ vattn_status vattn_execute_exact_grid(vattn_plan_t p, int B, const void* q, cons
   if (n_tiles < 0 || (n_tiles > 0 && !tile_map) || !aligned(tile_map, 4))
     return VATTN_ERR_INVALID_ARG;
   if (B == 0 || n_tiles == 0) return VATTN_OK;
-  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, tile_map, n_tiles, stream);
+  return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, tile_map, n_tiles,
+             packed_strides(p->info), stream);
 }
 
 vattn_status vattn_padding_mask(const int32_t* cu_seqlens, int B, int max_seqlen, uint8_t* mask,

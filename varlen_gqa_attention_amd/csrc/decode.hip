@@ -115,7 +115,7 @@ __device__ __forceinline__ void pipeline_tiles(int w, int ntiles, Buf& A, Buf& B
 
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int qrow, int hq, int d, float val) {
   __bf16 ob = (__bf16)val;
-  a.out[((int64_t)qrow * a.Hq + hq) * a.D + d] = __builtin_bit_cast(uint16_t, ob);
+  a.out[(int64_t)qrow * a.o_rs + (int64_t)hq * a.D + d] = __builtin_bit_cast(uint16_t, ob);
 }
 
 // Writes O = 0, LSE = -inf (no visible key) for heads [h0, h0 + nh).
@@ -238,7 +238,7 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
       u32x2 ov;
       ov[0] = pack_bf16x2(O[0] * inv, O[1] * inv);
       ov[1] = pack_bf16x2(O[2] * inv, O[3] * inv);
-      *reinterpret_cast<u32x2*>(a.out + ((int64_t)qrow * a.Hq + hq) * D + d) = ov;
+      *reinterpret_cast<u32x2*>(a.out + (int64_t)qrow * a.o_rs + hq * D + d) = ov;
       if (d == 0)
         a.lse[(int64_t)qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
     } else {
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 x = {0, 0, 0, 0};
-    if (hl < nh) x = ld16(a.q + ((int64_t)qrow * a.Hq + h0 + hl) * D + 32 * ks + 8 * g4);
+    if (hl < nh) x = ld16(a.q + (int64_t)qrow * a.q_rs + (h0 + hl) * D + 32 * ks + 8 * g4);
     qv[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
@@ -332,9 +332,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint8_t* vst = lds + w * TILE * D * 2;
-  const int64_t kvstride = (int64_t)a.Hkv * D;
-  const uint16_t* kbase = a.k + ((int64_t)sk.start * a.Hkv + u.hk) * D;
-  const uint16_t* vbase = a.v + ((int64_t)sk.start * a.Hkv + u.hk) * D;
+  const int64_t krs = a.k_rs, vrs = a.v_rs;
+  const uint16_t* kbase = a.k + (int64_t)sk.start * krs + u.hk * D;
+  const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + u.hk * D;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + TILE - 1) / TILE : 0;
 
   auto load_tile = [&](int t, u32x4 (&kr)[2][KS], u32x4 (&vr)[DV]) {
@@ -343,13 +343,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       const int key = min(key0 + 16 * kb2 + hl, kend - 1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = ld16(kbase + key * kvstride + 32 * ks + 8 * g4);
+      for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = ld16(kbase + key * krs + 32 * ks + 8 * g4);
     }
 #pragma unroll
     for (int i = 0; i < DV; ++i) {
       const int qi = i * 64 + lane;
       const int key = min(key0 + qi / CPR, kend - 1);
-      vr[i] = ld16(vbase + key * kvstride + 8 * (qi % CPR));
+      vr[i] = ld16(vbase + key * vrs + 8 * (qi % CPR));
     }
   };
 
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
     qw[g] = u32x4{0, 0, 0, 0};
-    if (g < nh) qw[g] = ld16(a.q + ((int64_t)qrow * a.Hq + h0 + g) * D + 8 * c);
+    if (g < nh) qw[g] = ld16(a.q + (int64_t)qrow * a.q_rs + (h0 + g) * D + 8 * c);
   }
   float m[GM], l[GM], o[GM][8];
 #pragma unroll
@@ -490,9 +490,9 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
   }
-  const int64_t kvstride = (int64_t)a.Hkv * D;
-  const uint16_t* kbase = a.k + ((int64_t)sk.start * a.Hkv + u.hk) * D + 8 * c;
-  const uint16_t* vbase = a.v + ((int64_t)sk.start * a.Hkv + u.hk) * D + 8 * c;
+  const int64_t krs = a.k_rs, vrs = a.v_rs;
+  const uint16_t* kbase = a.k + (int64_t)sk.start * krs + u.hk * D + 8 * c;
+  const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + u.hk * D + 8 * c;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + TILE - 1) / TILE : 0;
 
   auto load_tile = [&](int t, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
@@ -500,8 +500,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int key = min(key0 + i * RPI + r, kend - 1);
-      kr[i] = ld16(kbase + key * kvstride);
-      vr[i] = ld16(vbase + key * kvstride);
+      kr[i] = ld16(kbase + key * krs);
+      vr[i] = ld16(vbase + key * vrs);
     }
   };
 

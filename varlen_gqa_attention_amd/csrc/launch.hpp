@@ -22,6 +22,7 @@ struct DecodeArgs {
   int nsplit, chunk_keys;
   int s_max_q, s_max_kv;
   int64_t q_rows, kv_rows;
+  int64_t q_rs, k_rs, v_rs, o_rs;  // row (token) strides of q, k, v, out in elements
   float c;          // softmax scale * log2(e)
   int direct;       // 1: normalise and write out/lse; 0: write partials
   int fused;        // with direct == 0: 1 = last split workgroup merges, 0 = combine kernel
@@ -48,6 +49,7 @@ struct PrefillArgs {
   int n_qtiles;  // ceil(s_max_q / tq)
   int s_max_q, s_max_kv;
   int64_t q_rows, kv_rows;
+  int64_t q_rs, k_rs, v_rs, o_rs;  // row (token) strides of q, k, v, out in elements
   float c;
   int causal;
 };

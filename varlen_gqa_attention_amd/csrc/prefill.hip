@@ -102,7 +102,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const uint16_t* qp =
-        a.q + ((int64_t)(sq.start + tok[rb]) * a.Hq + hq[rb]) * D + 8 * (lane >> 5);
+        a.q + (int64_t)(sq.start + tok[rb]) * a.q_rs + hq[rb] * D + 8 * (lane >> 5);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = {0, 0, 0, 0};
@@ -128,9 +128,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
       for (int j = 0; j < 16; ++j) o[rb][i][j] = 0.f;
   }
 
-  const int64_t kvstride = (int64_t)a.Hkv * D;
-  const uint16_t* kbase = a.k + ((int64_t)sk.start * a.Hkv + hk) * D;
-  const uint16_t* vbase = a.v + ((int64_t)sk.start * a.Hkv + hk) * D;
+  const int64_t krs = a.k_rs, vrs = a.v_rs;
+  const uint16_t* kbase = a.k + (int64_t)sk.start * krs + hk * D;
+  const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + hk * D;
   const int ntiles = (kend + BN - 1) / BN;
 
   // Tiles reach LDS through registers: the loads of tile jt + 2 are issued
@@ -145,9 +145,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
       const int q = threadIdx.x + i * C::THREADS;
       if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
       const int r = q / CPR, c = q % CPR;
-      const int64_t off = (int64_t)min(jt * BN + r, kend - 1) * kvstride + 8 * c;
-      stk[i] = ld16(kbase + off);
-      stv[i] = ld16(vbase + off);
+      const int64_t key = min(jt * BN + r, kend - 1);
+      stk[i] = ld16(kbase + key * krs + 8 * c);
+      stv[i] = ld16(vbase + key * vrs + 8 * c);
     }
   };
   auto store_tile = [&](int jt) {
@@ -318,7 +318,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
     const float lt = l[rb] + xor_lane(l[rb], 32);
     if (!row_ok[rb]) continue;
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-    uint16_t* op = a.out + ((int64_t)(sq.start + tok[rb]) * a.Hq + hq[rb]) * D + 4 * (lane >> 5);
+    uint16_t* op = a.out + (int64_t)(sq.start + tok[rb]) * a.o_rs + hq[rb] * D + 4 * (lane >> 5);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
