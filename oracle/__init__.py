@@ -28,7 +28,8 @@ Sources (web pages), cited in the modules by the short tags below:
                MMA decode header, dispatch_decode, prefill tiling).
 
 Modules:
-  attention  fp64 varlen GQA attention, split partials and the LSE merge
+  attention  fp64 varlen GQA attention, split partials and the LSE merge,
+             attention over gathered (index-listed) keys
   brute      scalar pure-Python triple loops (tiny inputs only; a pin)
   mask       padding mask: vectorised formula and the per-sequence loop form
   chooser    plan-time split-count / grid rule

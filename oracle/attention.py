@@ -275,3 +275,47 @@ def attend_selected(q, k, v, cu_q, cu_kv, causal, picks, scale=None):
                             np.asarray(v[k0:k0 + Lk, hk, :], dtype=np.float64), vis, scale)
         res.append((q0 + i, h, o[0], ls[0]))
     return res
+
+
+def attend_gathered(q, k, v, cu_q, cu_idx, kv_idx, B, scale=None, s_max_q=None,
+                    s_max_kv=None, kv_rows=None):
+    """Attention over gathered keys (split-K blog post, The Context: Why
+    Split-K Matters -- each query head attends to a selected list of cached
+    tokens): sequence b's query rows cu_q[b]..cu_q[b+1] attend, without
+    causal masking, to the K/V rows kv_idx[cu_idx[b] .. cu_idx[b+1]) in that
+    list's order (a row listed twice counts twice). Reading for invalid data,
+    as for lengths: a row index outside [0, kv_rows) is clamped into range
+    and reported. Returns (out, lse, written, index_clamped).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    kv_idx = np.asarray(kv_idx, dtype=np.int64)
+    Tq, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if kv_rows is None:
+        kv_rows = k.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.full((Tq, Hq, D), np.nan)
+    lse = np.full((Tq, Hq), np.nan)
+    written = np.zeros(Tq, dtype=bool)
+    clamped_any = False
+    q0s, Lqs, _ = _lengths(cu_q, B, s_max_q)
+    i0s, Lks, _ = _lengths(cu_idx, B, s_max_kv)
+    for b in range(B):
+        q0, Lq, i0, Lk = int(q0s[b]), int(Lqs[b]), int(i0s[b]), int(Lks[b])
+        if Lq == 0:
+            continue
+        rows = kv_idx[i0:i0 + Lk]
+        bad = (rows < 0) | (rows >= kv_rows)
+        clamped_any = clamped_any or bool(bad.any())
+        rows = np.clip(rows, 0, kv_rows - 1)
+        vis = np.ones((Lq, Lk), dtype=bool)
+        for h in range(Hq):
+            hk = kv_head_of(h, Hq, Hkv)
+            o, ls = attend_rows(q[q0:q0 + Lq, h, :], k[rows, hk, :], v[rows, hk, :], vis, scale)
+            out[q0:q0 + Lq, h, :] = o
+            lse[q0:q0 + Lq, h] = ls
+        written[q0:q0 + Lq] = True
+    return out, lse, written, clamped_any

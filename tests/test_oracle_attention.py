@@ -331,3 +331,75 @@ def test_bf16_rounding_is_single_rounding_of_fp64():
     assert round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
     assert round_bf16(np.array([3.5e38]))[0] == np.inf
     assert round_bf16(np.array([2.0 ** -133]))[0] == 2.0 ** -133
+
+
+
+def _gather_case(rng, B, Hq, Hkv, D, n_rows, max_sel, dup=True):
+    q_lens = rng.integers(0, 3, size=B)
+    sel = rng.integers(0, max_sel + 1, size=B)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    cu_idx = np.concatenate([[0], np.cumsum(sel)]).astype(np.int64)
+    idx = rng.integers(0, n_rows, size=int(cu_idx[-1]))
+    if dup and idx.size > 2:
+        idx[1] = idx[0]
+    q = rng.standard_normal((max(1, int(cu_q[-1])), Hq, D))
+    k = rng.standard_normal((n_rows, Hkv, D))
+    v = rng.standard_normal((n_rows, Hkv, D))
+    return q, k, v, cu_q, cu_idx, idx
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_gathered_matches_brute_force_on_gathered_copies(seed):
+    """Gathering then attending equals the scalar triple loops run on
+    contiguous copies of the gathered rows (duplicates included)."""
+    rng = np.random.default_rng([9, seed])
+    Hkv, G = int(rng.choice([1, 2])), int(rng.choice([1, 2]))
+    Hq, D, B = Hkv * G, 4, int(rng.integers(1, 4))
+    q, k, v, cu_q, cu_idx, idx = _gather_case(rng, B, Hq, Hkv, D, 9, 6)
+    out, lse, written, clamped = A.attend_gathered(q, k, v, cu_q, cu_idx, idx, B)
+    assert not clamped
+    kg, vg = k[idx], v[idx]
+    ref = brute.attend_scalar(q.tolist(), kg.tolist(), vg.tolist(), cu_q, cu_idx, B, False)
+    assert written.sum() == len(ref) // Hq
+    for (row, h), (o, ls) in ref.items():
+        np.testing.assert_allclose(out[row, h], o, rtol=1e-12, atol=1e-12)
+        if math.isinf(ls):
+            assert lse[row, h] == -np.inf
+        else:
+            assert abs(lse[row, h] - ls) <= 1e-12 * max(1.0, abs(ls))
+
+
+def test_identity_gather_equals_contiguous_attention():
+    rng = np.random.default_rng(11)
+    q, k, v, cu_q, cu_k = _rand_case(rng, 3, 4, 2, 8, 2, 9, False)
+    idx = np.arange(int(cu_k[3]))
+    o1, l1, w1, _ = A.attend_gathered(q, k, v, cu_q, cu_k[:4], idx, 3)
+    o2, l2, w2 = A.attend_varlen(q, k, v, cu_q, cu_k, 3, False)
+    assert (w1 == w2).all()
+    np.testing.assert_allclose(o1[w1], o2[w2], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1[w1], l2[w2], rtol=1e-12, atol=1e-12)
+
+
+def test_gathered_is_invariant_to_index_order():
+    rng = np.random.default_rng(12)
+    q, k, v, cu_q, cu_idx, idx = _gather_case(rng, 3, 4, 2, 8, 20, 7)
+    o1, l1, w, _ = A.attend_gathered(q, k, v, cu_q, cu_idx, idx, 3)
+    perm = idx.copy()
+    for b in range(3):
+        a, e = int(cu_idx[b]), int(cu_idx[b + 1])
+        perm[a:e] = rng.permutation(perm[a:e])
+    o2, l2, _, _ = A.attend_gathered(q, k, v, cu_q, cu_idx, perm, 3)
+    np.testing.assert_allclose(o1[w], o2[w], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l1[w], l2[w], rtol=1e-12, atol=1e-12)
+
+
+def test_gathered_clamps_out_of_range_rows():
+    rng = np.random.default_rng(13)
+    q, k, v, _, _, _ = _gather_case(rng, 1, 2, 1, 8, 10, 4)
+    cu_q = np.array([0, 1])
+    cu_idx = np.array([0, 3])
+    o1, l1, _, c1 = A.attend_gathered(q, k, v, cu_q, cu_idx, np.array([-5, 4, 99]), 1)
+    o2, l2, _, c2 = A.attend_gathered(q, k, v, cu_q, cu_idx, np.array([0, 4, 9]), 1)
+    assert c1 and not c2
+    np.testing.assert_array_equal(o1[:1], o2[:1])
+    np.testing.assert_array_equal(l1[:1], l2[:1])
