@@ -390,6 +390,39 @@ def mask_measure():
                 us=round(sorted(per)[len(per) // 2] * 1e3, 2))
 
 
+def gathered_measure(steps=50):
+    """Decode over gathered keys: 16 sequences, each attending 2048 rows
+    selected (sorted, without repeats) from its own 32768-token history."""
+    torch = _torch()
+    import numpy as np
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    B, Hq, Hkv, D, hist, sel = 16, 32, 8, 128, 32768, 2048
+    plan = V.Plan(B, 1, sel, Hq, Hkv, D, False)
+    q = I.normal_bf16((B, Hq, D), 40, "cuda")
+    k = I.normal_bf16((B * hist, Hkv, D), 41, "cuda")
+    v = I.normal_bf16((B * hist, Hkv, D), 42, "cuda")
+    rng = I.rng(7, 0)
+    idx = np.concatenate([b * hist + np.sort(rng.choice(hist, sel, replace=False))
+                          for b in range(B)]).astype(np.int32)
+    kv_idx = torch.from_numpy(idx).cuda()
+    cu_q = torch.from_numpy(I.cu_from_lengths(np.ones(B, np.int64))).cuda()
+    cu_idx = torch.from_numpy(I.cu_from_lengths(np.full(B, sel))).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device="cuda")
+    f = lambda: plan.gathered(q, k, v, cu_q, cu_idx, kv_idx, out=out, lse=lse, B=B)
+    g = capture(f)
+    total, _ = time_replays([g.replay], steps, 5)
+    ms = total / steps
+    kv_bytes = B * sel * Hkv * D * 2 * 2
+    return dict(workload=f"gathered-key decode: B={B}, Hq={Hq}, Hkv={Hkv}, D={D}, {sel} keys per "
+                         f"sequence selected from {hist} (sorted, seed 7), graph replay",
+                us_per_step=round(ms * 1e3, 2), kv_gbs=round(kv_bytes / (ms * 1e-3) / 1e9, 1),
+                frac_hbm_peak=round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                nsplit=plan.info["nsplit"],
+                decode_path=("mfma" if plan.info["decode_path"] == 2 else "wave"))
+
+
 def calibrate_copy():
     """Plain elementwise copy of a known size, for scaling HBM counters."""
     torch = _torch()
@@ -451,6 +484,7 @@ def main():
     if not args.no_secondary:
         line["prefill"] = prefill_measure(args)
         line["batched_decode"] = batched_decode_measure(args)
+        line["gathered_decode"] = gathered_measure()
         line["padding_mask"] = mask_measure()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)

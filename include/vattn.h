@@ -74,6 +74,7 @@ typedef enum {
 #define VATTN_ERRBIT_Q_LEN   0x1 /* some query length outside [0, s_max_q] was clamped */
 #define VATTN_ERRBIT_KV_LEN  0x2 /* some KV length outside [0, s_max_kv] was clamped */
 #define VATTN_ERRBIT_ROWS    0x4 /* a sequence ran past q_rows / kv_rows and was cut */
+#define VATTN_ERRBIT_INDEX   0x8 /* a gathered K/V row index outside [0, kv_rows) was clamped */
 
 typedef struct vattn_plan_s* vattn_plan_t;
 
@@ -179,6 +180,28 @@ vattn_status vattn_execute(vattn_plan_t p, int B,
                            void* out, float* lse,
                            int64_t q_rows, int64_t kv_rows,
                            vattn_stream_t stream);
+
+/*
+ * Decode over gathered keys (split-K blog post, The Context: Why Split-K
+ * Matters and The Message: each query head attends to a selected list of
+ * cached tokens, e.g. top-k indices or page-indexed KV): sequence b's query
+ * row attends to the K/V rows kv_idx[cu_idx[b] .. cu_idx[b+1]) of k and v
+ * ([kv_rows, Hkv, D], packed), in any order, with no causal mask; a row
+ * listed twice counts twice. Uses the decode plan's split rule with
+ * s_max_kv = the longest list, the same split partials and the LSE combine
+ * (the combine kernel also for plans made with fuse_combine = 1). A list
+ * length outside [0, s_max_kv] is clamped and flagged as for cu_seqlens_kv
+ * (n_idx, the capacity of kv_idx, plays the role of kv_rows); a row index
+ * outside [0, kv_rows) is clamped into range and sets VATTN_ERRBIT_INDEX.
+ * Decode plans only (VATTN_ERR_UNSUPPORTED otherwise); kv_idx is an int32
+ * device array, 4-byte aligned. Enqueue-only, like vattn_execute.
+ */
+vattn_status vattn_execute_gathered(vattn_plan_t p, int B,
+                                    const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_idx,
+                                    const int32_t* kv_idx, void* out, float* lse,
+                                    int64_t q_rows, int64_t kv_rows, int64_t n_idx,
+                                    vattn_stream_t stream);
 
 /*
  * vattn_execute on token-row-strided views (cudnn-frontend issue #552,

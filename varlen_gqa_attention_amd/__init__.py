@@ -16,7 +16,7 @@ import ctypes
 
 from . import _lib
 from ._lib import (DECODE_AUTO, DECODE_MFMA, DECODE_WAVE, ERRBIT_KV_LEN, ERRBIT_Q_LEN,
-                   ERRBIT_ROWS, PlanInfo, PlanOpts, VattnError)
+                   ERRBIT_INDEX, ERRBIT_ROWS, PlanInfo, PlanOpts, VattnError)
 
 
 class _LazyLib:
@@ -29,7 +29,8 @@ class _LazyLib:
 _LIB = _LazyLib()
 
 __all__ = ["Plan", "padding_mask", "cross_padding_masks", "describe_plan", "VattnError", "DECODE_AUTO",
-           "DECODE_WAVE", "DECODE_MFMA", "ERRBIT_Q_LEN", "ERRBIT_KV_LEN", "ERRBIT_ROWS"]
+           "DECODE_WAVE", "DECODE_MFMA", "ERRBIT_Q_LEN", "ERRBIT_KV_LEN", "ERRBIT_ROWS",
+           "ERRBIT_INDEX"]
 
 
 def _opts(target_blocks_per_cu=0, nsplit_cap=0, force_nsplit=0, force_decode_path=0,
@@ -123,6 +124,28 @@ class Plan:
                 self._h, B, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out), out.stride(0), _ptr(lse),
                 q.shape[0], k.shape[0], _stream_of(q, stream)), "vattn_execute_strided")
+        return out, lse
+
+    def gathered(self, q, k, v, cu_seqlens_q, cu_idx, kv_idx, out=None, lse=None, B=None,
+                 stream=None):
+        """Decode over gathered keys: sequence b attends K/V rows
+        kv_idx[cu_idx[b]:cu_idx[b+1]] (int32 device tensors)."""
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        if B is None:
+            B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_q.numel() < B + 1 or cu_idx.numel() < B + 1:
+            raise ValueError("cu_seqlens_q and cu_idx need at least B + 1 entries")
+        self._check(q, k, v, cu_seqlens_q, cu_idx, out, lse)
+        if kv_idx.dtype != torch.int32 or not kv_idx.is_cuda or not kv_idx.is_contiguous():
+            raise ValueError("kv_idx must be a contiguous int32 device tensor")
+        _lib.check(_LIB.vattn_execute_gathered(
+            self._h, B, _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_idx),
+            _ptr(kv_idx), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], kv_idx.numel(),
+            _stream_of(q, stream)), "vattn_execute_gathered")
         return out, lse
 
     def execute_exact_grid(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, tile_map, out, lse, B,

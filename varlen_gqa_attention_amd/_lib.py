@@ -18,12 +18,13 @@ VATTN_ERR_HIP = -3
 VATTN_ERR_OOM = -4
 
 DECODE_AUTO, DECODE_WAVE, DECODE_MFMA = 0, 1, 2
-ERRBIT_Q_LEN, ERRBIT_KV_LEN, ERRBIT_ROWS = 0x1, 0x2, 0x4
+ERRBIT_Q_LEN, ERRBIT_KV_LEN, ERRBIT_ROWS, ERRBIT_INDEX = 0x1, 0x2, 0x4, 0x8
 
 # every symbol include/vattn.h declares
 EXPORTS = (
     "vattn_status_string", "vattn_abi_version", "vattn_plan", "vattn_plan_ex",
-    "vattn_plan_describe", "vattn_plan_query", "vattn_execute", "vattn_execute_strided",
+    "vattn_plan_describe", "vattn_plan_query", "vattn_execute", "vattn_execute_gathered",
+    "vattn_execute_strided",
     "vattn_execute_exact_grid", "vattn_padding_mask", "vattn_cross_padding_mask",
     "vattn_plan_error_word",
     "vattn_plan_read_error", "vattn_plan_clear_error", "vattn_plan_set_kernel_events",
@@ -88,6 +89,9 @@ def load():
     L.vattn_plan_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
     L.vattn_execute.restype = c_int
     L.vattn_execute.argtypes = [vp, c_int, vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64, vp]
+    L.vattn_execute_gathered.restype = c_int
+    L.vattn_execute_gathered.argtypes = [vp, c_int, vp, vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64,
+                                         c_i64, vp]
     L.vattn_execute_strided.restype = c_int
     L.vattn_execute_strided.argtypes = [vp, c_int, vp, c_i64, vp, c_i64, vp, c_i64, vp, vp, vp,
                                         c_i64, vp, c_i64, c_i64, vp]

@@ -162,10 +162,17 @@ static Strides packed_strides(const vattn_plan_info& in) {
                  (int64_t)in.Hq * in.D};
 }
 
+// Gathered keys for decode: the index list and the K/V row count (null: none).
+struct Gather {
+  const int32_t* idx;
+  int64_t bound;
+};
+
 static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
                         const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
                         int64_t q_rows, int64_t kv_rows, const int32_t* tile_map, int n_map,
-                        const Strides& rs, vattn_stream_t stream) {
+                        const Strides& rs, vattn_stream_t stream,
+                        const Gather& gather = Gather{nullptr, 0}) {
   const vattn_plan_info& in = p->info;
   const float c = (float)(1.0 / std::sqrt((double)in.D) * 1.4426950408889634);
   hipStream_t st = (hipStream_t)stream;
@@ -207,7 +214,14 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.c = c;
     a.direct = in.direct;
     a.fused = in.fused_combine;
-    e = vattn::launch_decode(a, in.decode_path, in.threads / 64, in.grid, in.combine_grid,
+    a.kv_idx = gather.idx;
+    a.kv_bound = gather.bound;
+    int combine_grid = in.combine_grid;
+    if (gather.idx && in.fused_combine) {  // gathered keys merge in the combine kernel
+      a.fused = 0;
+      combine_grid = in.B_max * in.Hq;
+    }
+    e = vattn::launch_decode(a, in.decode_path, in.threads / 64, in.grid, combine_grid,
                              st, p->ev_start, p->ev_stop);
   } else {
     vattn::PrefillArgs a;
@@ -261,6 +275,21 @@ vattn_status vattn_execute(vattn_plan_t p, int B, const void* q, const void* k, 
   if (st != VATTN_OK || B == 0) return st;
   return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, nullptr, 0,
              packed_strides(p->info), stream);
+}
+
+vattn_status vattn_execute_gathered(vattn_plan_t p, int B, const void* q, const void* k,
+                                    const void* v, const int32_t* cu_q, const int32_t* cu_idx,
+                                    const int32_t* kv_idx, void* out, float* lse, int64_t q_rows,
+                                    int64_t kv_rows, int64_t n_idx, vattn_stream_t stream) {
+  // row-capacity checks apply to q (q_rows) and to the index list (n_idx)
+  vattn_status st = check_exec(p, B, q, k, v, cu_q, cu_idx, out, lse, q_rows, n_idx);
+  if (st != VATTN_OK) return st;
+  if (!p->info.is_decode) return VATTN_ERR_UNSUPPORTED;
+  if (kv_rows < 1 || kv_rows > INT32_MAX) return VATTN_ERR_INVALID_ARG;
+  if (B == 0) return VATTN_OK;
+  if (!kv_idx || !aligned(kv_idx, 4)) return VATTN_ERR_INVALID_ARG;
+  return run(p, B, q, k, v, cu_q, cu_idx, out, lse, q_rows, n_idx, nullptr, 0,
+             packed_strides(p->info), stream, Gather{kv_idx, kv_rows});
 }
 
 vattn_status vattn_execute_strided(vattn_plan_t p, int B, const void* q, int64_t q_row_stride,

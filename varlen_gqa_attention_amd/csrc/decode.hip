@@ -283,7 +283,7 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
 // ---------------------------------------------------------------------------
 // MFMA path
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool FUSED>
+template <int D, int NW, bool FUSED, bool GATHER>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;     // 32-wide k-steps of Q K^T
   constexpr int DB = D / 16;     // 16-wide d blocks of P V
@@ -333,24 +333,59 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 
   uint8_t* vst = lds + w * TILE * D * 2;
   const int64_t krs = a.k_rs, vrs = a.v_rs;
-  const uint16_t* kbase = a.k + (int64_t)sk.start * krs + u.hk * D;
-  const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + u.hk * D;
+  // contiguous keys: row = key (bases offset to the sequence); gathered keys:
+  // row = kv_idx[sk.start + key]
+  const int64_t seq_row = GATHER ? 0 : sk.start;
+  const uint16_t* kbase = a.k + seq_row * krs + u.hk * D;
+  const uint16_t* vbase = a.v + seq_row * vrs + u.hk * D;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + TILE - 1) / TILE : 0;
+  int gflags = 0;
+  auto row_of = [&](int idx_or_key) -> int64_t {
+    if constexpr (GATHER) {
+      int r = idx_or_key;
+      if (r < 0 || r >= a.kv_bound) {
+        gflags = kErrIndex;
+        r = r < 0 ? 0 : (int)(a.kv_bound - 1);
+      }
+      return r;
+    } else {
+      return idx_or_key;
+    }
+  };
 
-  auto load_tile = [&](int t, u32x4 (&kr)[2][KS], u32x4 (&vr)[DV]) {
+  // Gathered keys: each register buffer also holds the row indices of the
+  // tile it loads next (fetched when it issues its current tile, 2 NW tiles
+  // ahead), so no K/V load waits on an index load issued after other tiles.
+  struct TileRegs {
+    u32x4 k[2][KS], v[DV];
+    int rk[GATHER ? 2 : 1], rv[GATHER ? DV : 1];
+  } A, B;
+  auto fetch_rows = [&](int t, TileRegs& r) {
+    if constexpr (GATHER) {
+      const int key0 = kbeg + t * TILE;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        r.rk[kb2] = a.kv_idx[sk.start + min(key0 + 16 * kb2 + hl, kend - 1)];
+#pragma unroll
+      for (int i = 0; i < DV; ++i)
+        r.rv[i] = a.kv_idx[sk.start + min(key0 + (i * 64 + lane) / CPR, kend - 1)];
+    }
+  };
+  auto load_tile = [&](int t, TileRegs& r) {
     const int key0 = kbeg + t * TILE;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int key = min(key0 + 16 * kb2 + hl, kend - 1);
+      const int64_t row = row_of(GATHER ? r.rk[kb2] : min(key0 + 16 * kb2 + hl, kend - 1));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[kb2][ks] = ld16(kbase + key * krs + 32 * ks + 8 * g4);
+      for (int ks = 0; ks < KS; ++ks) r.k[kb2][ks] = ld16(kbase + row * krs + 32 * ks + 8 * g4);
     }
 #pragma unroll
     for (int i = 0; i < DV; ++i) {
       const int qi = i * 64 + lane;
-      const int key = min(key0 + qi / CPR, kend - 1);
-      vr[i] = ld16(vbase + key * vrs + 8 * (qi % CPR));
+      const int64_t row = row_of(GATHER ? r.rv[i] : min(key0 + qi / CPR, kend - 1));
+      r.v[i] = ld16(vbase + row * vrs + 8 * (qi % CPR));
     }
+    fetch_rows(t + 2 * NW, r);
   };
 
   auto process_tile = [&](int t, const u32x4 (&kr)[2][KS], const u32x4 (&vr)[DV]) {
@@ -423,11 +458,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     wave_lds_sync();
   };
 
-  struct TileRegs {
-    u32x4 k[2][KS], v[DV];
-  } A, B;
-  pipeline_tiles<NW>(w, ntiles, A, B, [&](int t, TileRegs& r) { load_tile(t, r.k, r.v); },
+  if (w < ntiles) {
+    fetch_rows(w, A);
+    fetch_rows(w + (w + NW < ntiles ? NW : 0), B);
+  }
+  pipeline_tiles<NW>(w, ntiles, A, B, [&](int t, TileRegs& r) { load_tile(t, r); },
                      [&](int t, TileRegs& r) { process_tile(t, r.k, r.v); });
+  if constexpr (GATHER) report(a.err, gflags);
   // l: each lane summed its own 8 keys per tile; add the four key groups
   l += xor_lane(l, 16);
   l += xor_lane(l, 32);
@@ -446,7 +483,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Wave (VALU) path for small G
 // ---------------------------------------------------------------------------
-template <int D, int NW, int GM, bool FUSED>
+template <int D, int NW, int GM, bool FUSED, bool GATHER>
 __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   constexpr int LPR = D / 8;             // lanes per key row (8 d-values each)
   constexpr int RPI = 64 / LPR;          // key rows per load instruction
@@ -491,18 +528,38 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
   }
   const int64_t krs = a.k_rs, vrs = a.v_rs;
-  const uint16_t* kbase = a.k + (int64_t)sk.start * krs + u.hk * D + 8 * c;
-  const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + u.hk * D + 8 * c;
+  const int64_t seq_row = GATHER ? 0 : sk.start;  // gathered: rows come from kv_idx
+  const uint16_t* kbase = a.k + seq_row * krs + u.hk * D + 8 * c;
+  const uint16_t* vbase = a.v + seq_row * vrs + u.hk * D + 8 * c;
   const int ntiles = (kend > kbeg) ? (kend - kbeg + TILE - 1) / TILE : 0;
+  int gflags = 0;
 
-  auto load_tile = [&](int t, u32x4 (&kr)[NI], u32x4 (&vr)[NI]) {
+  // gathered keys: the row indices of a buffer's next tile are fetched when
+  // it issues its current one (as in the MFMA path)
+  auto fetch_rows = [&](int t, int (&ix)[NI]) {
+    if constexpr (GATHER) {
+      const int key0 = kbeg + t * TILE;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) ix[i] = a.kv_idx[sk.start + min(key0 + i * RPI + r, kend - 1)];
+    }
+  };
+  auto load_tile = [&](int t, u32x4 (&kr)[NI], u32x4 (&vr)[NI], int (&ix)[NI], int t_next) {
     const int key0 = kbeg + t * TILE;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int key = min(key0 + i * RPI + r, kend - 1);
-      kr[i] = ld16(kbase + key * krs);
-      vr[i] = ld16(vbase + key * vrs);
+      int64_t row = min(key0 + i * RPI + r, kend - 1);
+      if constexpr (GATHER) {
+        int rr = ix[i];
+        if (rr < 0 || rr >= a.kv_bound) {
+          gflags = kErrIndex;
+          rr = rr < 0 ? 0 : (int)(a.kv_bound - 1);
+        }
+        row = rr;
+      }
+      kr[i] = ld16(kbase + row * krs);
+      vr[i] = ld16(vbase + row * vrs);
     }
+    fetch_rows(t_next, ix);
   };
 
   auto process_tile = [&](int t, const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
@@ -564,21 +621,25 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   };
 
   u32x4 kA[NI], vA[NI], kB[NI], vB[NI];
+  int ixA[NI], ixB[NI];
   // Two tiles in flight with unconditional loads, as in pipeline_tiles, but
   // one loop: past the wave's last tile the loads re-read that tile (cached).
   // This path runs long sequences (many tiles per wave), where the re-reads
   // are negligible, and the compact loop keeps register use low.
   if (w < ntiles) {
     const int tl = w + NW * ((ntiles - 1 - w) / NW);
-    load_tile(w, kA, vA);
-    load_tile(min(w + NW, tl), kB, vB);
+    fetch_rows(w, ixA);
+    fetch_rows(min(w + NW, tl), ixB);
+    load_tile(w, kA, vA, ixA, min(w + 2 * NW, tl));
+    load_tile(min(w + NW, tl), kB, vB, ixB, min(w + 3 * NW, tl));
     for (int t = w; t < ntiles; t += 2 * NW) {
       process_tile(t, kA, vA);
-      load_tile(min(t + 2 * NW, tl), kA, vA);
+      load_tile(min(t + 2 * NW, tl), kA, vA, ixA, min(t + 4 * NW, tl));
       if (t + NW < ntiles) process_tile(t + NW, kB, vB);
-      load_tile(min(t + 3 * NW, tl), kB, vB);
+      load_tile(min(t + 3 * NW, tl), kB, vB, ixB, min(t + 5 * NW, tl));
     }
   }
+  if constexpr (GATHER) report(a.err, gflags);
   // add the row groups' partial sums (their m are identical)
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
@@ -636,27 +697,29 @@ static void launch_timed(Kern kern, int grid, int threads, hipStream_t st, hipEv
   else kern<<<grid, threads, 0, st>>>(a);
 }
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool GATHER>
 static void launch_split(const DecodeArgs& a, int path, int nw, int grid, hipStream_t st,
                          hipEvent_t ev0, hipEvent_t ev1) {
   // 8-wave workgroups only for D <= 128 (the plan never picks them above)
   if constexpr (D <= 128) {
     if (nw == 8) {
-      if (path == 2) launch_timed(decode_mfma_kernel<D, 8, FUSED>, grid, 512, st, ev0, ev1, a);
-      else launch_timed(decode_wave_kernel<D, 8, 4, FUSED>, grid, 512, st, ev0, ev1, a);
+      if (path == 2) launch_timed(decode_mfma_kernel<D, 8, FUSED, GATHER>, grid, 512, st, ev0, ev1, a);
+      else launch_timed(decode_wave_kernel<D, 8, 4, FUSED, GATHER>, grid, 512, st, ev0, ev1, a);
       return;
     }
   }
-  if (path == 2) launch_timed(decode_mfma_kernel<D, 4, FUSED>, grid, 256, st, ev0, ev1, a);
-  else launch_timed(decode_wave_kernel<D, 4, 4, FUSED>, grid, 256, st, ev0, ev1, a);
+  if (path == 2) launch_timed(decode_mfma_kernel<D, 4, FUSED, GATHER>, grid, 256, st, ev0, ev1, a);
+  else launch_timed(decode_wave_kernel<D, 4, 4, FUSED, GATHER>, grid, 256, st, ev0, ev1, a);
 }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
                                   hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  // the fused-merge code is compiled only into the kernels that use it
-  if (a.fused && !a.direct) launch_split<D, true>(a, path, nw, grid, st, ev0, ev1);
-  else launch_split<D, false>(a, path, nw, grid, st, ev0, ev1);
+  // the fused-merge and gathered-key code is compiled only into the kernels
+  // that use it (gathered keys always merge in the combine kernel)
+  if (a.kv_idx) launch_split<D, false, true>(a, path, nw, grid, st, ev0, ev1);
+  else if (a.fused && !a.direct) launch_split<D, true, false>(a, path, nw, grid, st, ev0, ev1);
+  else launch_split<D, false, false>(a, path, nw, grid, st, ev0, ev1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.fused) return e;
   decode_combine_kernel<D><<<combine_grid, D < 64 ? 64 : D, 0, st>>>(a);

@@ -21,6 +21,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kErrQLen = 0x1;
 constexpr int kErrKvLen = 0x2;
 constexpr int kErrRows = 0x4;
+constexpr int kErrIndex = 0x8;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

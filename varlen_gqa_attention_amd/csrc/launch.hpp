@@ -17,6 +17,11 @@ struct DecodeArgs {
   float2* part_ml;  // [B_max, Hq, nsplit] (m in log2 units, l)
   int32_t* err;
   int32_t* counters;  // [n_units] arrival counters of the fused merge (kept at 0 between launches)
+  // Gathered keys (null: contiguous): key j of sequence b is K/V row
+  // kv_idx[cu_kv[b] + j], clamped into [0, kv_bound); cu_kv then indexes the
+  // list and kv_rows is the list's capacity.
+  const int32_t* kv_idx;
+  int64_t kv_bound;
   int B, Hq, Hkv, G, D;
   int head_blocks;  // workgroups per (b, hk) along the head dimension
   int nsplit, chunk_keys;
