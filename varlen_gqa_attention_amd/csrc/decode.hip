@@ -419,8 +419,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         sc[kb2 * 4 + i] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, xor_lane(mx, 16));
-    mx = fmaxf(mx, xor_lane(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     const float mnew = fmaxf(m, mx);
     const float msub = (mnew == kNegInf) ? 0.f : mnew;
     const float alpha = fast_exp2(m - msub);
@@ -466,8 +465,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                      [&](int t, TileRegs& r) { process_tile(t, r.k, r.v); });
   if constexpr (GATHER) report(a.err, gflags);
   // l: each lane summed its own 8 keys per tile; add the four key groups
-  l += xor_lane(l, 16);
-  l += xor_lane(l, 32);
+  l = sum_xor32(sum_xor16(l));
 
   __syncthreads();  // staging area becomes the merge area
   float* mo = reinterpret_cast<float*>(lds);

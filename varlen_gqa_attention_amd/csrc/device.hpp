@@ -53,6 +53,42 @@ __device__ __forceinline__ float xor_lane(float x, int mask) {
       (lane ^ mask) << 2, __builtin_bit_cast(int, x)));
 }
 
+// Lanes 32 (or 16) apart through the gfx950 lane-swap instructions
+// (v_permlane32_swap / v_permlane16_swap): with both operands x, each lane
+// ends up holding the pair {x[lane], x[lane ^ 32]} (or ^ 16) across the two
+// registers, so a max or a sum of the two is the exchange-and-combine step of
+// a reduction without the LDS round trip of ds_bpermute. Written as inline
+// asm (a VALU op, no memory access) with two distinct read-write operands:
+// this hipcc's builtin for these instructions returns the second result from
+// the wrong register. The s_nop gives the wait states a swap needs after a
+// VALU write of its operands.
+__device__ __forceinline__ void lane_swap32(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lane_swap16(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  lane_swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a = x, b = x;
+  lane_swap32(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float a = x, b = x;
+  lane_swap16(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float a = x, b = x;
+  lane_swap16(a, b);
+  return a + b;
+}
+
 // Sum over aligned groups of N lanes (N in 1..64); every lane of the group
 // receives the group total.
 template <int N>
@@ -61,8 +97,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp<0x4E>(x);
   if constexpr (N >= 8) x += dpp<0x141>(x);
   if constexpr (N >= 16) x += dpp<0x140>(x);
-  if constexpr (N >= 32) x += xor_lane(x, 16);
-  if constexpr (N >= 64) x += xor_lane(x, 32);
+  if constexpr (N >= 32) x = sum_xor16(x);
+  if constexpr (N >= 64) x = sum_xor32(x);
   return x;
 }
 
@@ -73,8 +109,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp<0x141>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<0x140>(x));
-  if constexpr (N >= 32) x = fmaxf(x, xor_lane(x, 16));
-  if constexpr (N >= 64) x = fmaxf(x, xor_lane(x, 32));
+  if constexpr (N >= 32) x = max_xor16(x);
+  if constexpr (N >= 64) x = max_xor32(x);
   return x;
 }
 
@@ -86,8 +122,8 @@ __device__ __forceinline__ float across_groups_max(float x) {
   if constexpr (FROM <= 2) x = fmaxf(x, xor_lane(x, 2));
   if constexpr (FROM <= 4) x = fmaxf(x, xor_lane(x, 4));
   if constexpr (FROM <= 8) x = fmaxf(x, xor_lane(x, 8));
-  if constexpr (FROM <= 16) x = fmaxf(x, xor_lane(x, 16));
-  if constexpr (FROM <= 32) x = fmaxf(x, xor_lane(x, 32));
+  if constexpr (FROM <= 16) x = max_xor16(x);
+  if constexpr (FROM <= 32) x = max_xor32(x);
   return x;
 }
 template <int FROM>
@@ -96,8 +132,8 @@ __device__ __forceinline__ float across_groups_sum(float x) {
   if constexpr (FROM <= 2) x += xor_lane(x, 2);
   if constexpr (FROM <= 4) x += xor_lane(x, 4);
   if constexpr (FROM <= 8) x += xor_lane(x, 8);
-  if constexpr (FROM <= 16) x += xor_lane(x, 16);
-  if constexpr (FROM <= 32) x += xor_lane(x, 32);
+  if constexpr (FROM <= 16) x = sum_xor16(x);
+  if constexpr (FROM <= 32) x = sum_xor32(x);
   return x;
 }
 

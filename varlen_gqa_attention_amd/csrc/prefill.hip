@@ -231,7 +231,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][kb][i]);
-      mx = fmaxf(mx, xor_lane(mx, 32)) * a.c;   // row max in base-2 units
+      mx = max_xor32(mx) * a.c;   // row max in base-2 units
       // raise the reference max only when the row max grew by more than 2^8
       // (or the row had no reference yet); rescale O and l when it moves
       const bool grow = mx > m[rb] + 8.f;
@@ -315,7 +315,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   // ---- epilogue: lane holds O^T[d = 32 db + 8 (i/4) + 4 (lane>>5) + i%4][row]
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float lt = l[rb] + xor_lane(l[rb], 32);
+    const float lt = sum_xor32(l[rb]);
     if (!row_ok[rb]) continue;
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
     uint16_t* op = a.out + (int64_t)(sq.start + tok[rb]) * a.o_rs + hq[rb] * D + 4 * (lane >> 5);
