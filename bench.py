@@ -390,7 +390,7 @@ def mask_measure():
                 us=round(sorted(per)[len(per) // 2] * 1e3, 2))
 
 
-def gathered_measure(steps=50):
+def gathered_measure(steps=50, **plan_opts):
     """Decode over gathered keys: 16 sequences, each attending 2048 rows
     selected (sorted, without repeats) from its own 32768-token history."""
     torch = _torch()
@@ -398,7 +398,7 @@ def gathered_measure(steps=50):
     import varlen_gqa_attention_amd as V
     from varlen_gqa_attention_amd import inputs as I
     B, Hq, Hkv, D, hist, sel = 16, 32, 8, 128, 32768, 2048
-    plan = V.Plan(B, 1, sel, Hq, Hkv, D, False)
+    plan = V.Plan(B, 1, sel, Hq, Hkv, D, False, **plan_opts)
     q = I.normal_bf16((B, Hq, D), 40, "cuda")
     k = I.normal_bf16((B * hist, Hkv, D), 41, "cuda")
     v = I.normal_bf16((B * hist, Hkv, D), 42, "cuda")
@@ -448,13 +448,15 @@ def main():
     ap.add_argument("--decode-path", type=int, default=0, choices=[0, 1, 2])
     ap.add_argument("--fuse-combine", type=int, default=0, choices=[0, 1, 2])
     ap.add_argument("--nsplit-cap", type=int, default=0)
+    ap.add_argument("--target-blocks", type=int, default=0,
+                    help="decode split rule: workgroups per CU to aim for (0 = plan default)")
     ap.add_argument("--prefill-len", type=int, default=0,
                     help="with --workload prefill: give every sequence this length")
     ap.add_argument("--decode-waves", type=int, default=0, choices=[0, 4, 8])
     ap.add_argument("--graph-steps", type=int, default=0,
                     help="long decode: steps per captured graph (0 = one per K/V copy)")
     ap.add_argument("--workload", default="long_decode",
-                    choices=["long_decode", "prefill", "batched_decode"],
+                    choices=["long_decode", "prefill", "batched_decode", "gathered_decode"],
                     help="headline workload (default: long decode); the others are for "
                          "profiling runs")
     args = ap.parse_args()
@@ -462,7 +464,8 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is described in DESIGN.md, not built)"}))
         sys.exit(2)
-    args.plan_opts = dict(force_nsplit=args.force_nsplit, force_decode_path=args.decode_path,
+    args.plan_opts = dict(target_blocks_per_cu=args.target_blocks,
+                          force_nsplit=args.force_nsplit, force_decode_path=args.decode_path,
                           fuse_combine=args.fuse_combine, nsplit_cap=args.nsplit_cap,
                           decode_waves=args.decode_waves)
     torch = _torch()
@@ -470,6 +473,10 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.workload == "gathered_decode":
+        print(json.dumps({"workload": args.workload,
+                          **gathered_measure(**{k: v for k, v in args.plan_opts.items() if v})}))
         return
     if args.workload != "long_decode":
         fn = prefill_measure if args.workload == "prefill" else batched_decode_measure

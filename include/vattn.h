@@ -90,7 +90,7 @@ typedef struct vattn_plan_s* vattn_plan_t;
  * plan option here).
  */
 typedef struct {
-  int target_blocks_per_cu; /* default 2 */
+  int target_blocks_per_cu; /* default 8 */
   int nsplit_cap;           /* default 32 */
   int force_nsplit;         /* > 0: use this split count (capped by the tile count) */
   int force_decode_path;    /* VATTN_DECODE_* */

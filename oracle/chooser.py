@@ -32,15 +32,21 @@ def _cdiv(a, b):
 
 
 def choose_decode_split(B_max, s_max_kv, Hkv, n_cu, block_n,
-                        target_blocks_per_cu=2, nsplit_cap=32, force_nsplit=0):
-    """Returns dict(nsplit, chunk_tiles, chunk_keys, n_tiles, grid, direct)."""
+                        target_blocks_per_cu=2, nsplit_cap=32, force_nsplit=0,
+                        min_chunk_tiles=1):
+    """Returns dict(nsplit, chunk_tiles, chunk_keys, n_tiles, grid, direct).
+
+    The defaults are the pages' rule (about two blocks per SM, capped by the
+    tile count and 32). min_chunk_tiles > 1 adds a floor on the work per
+    split: at most ceil(n_tiles / min_chunk_tiles) splits.
+    """
     n_units = B_max * Hkv
     n_tiles = _cdiv(s_max_kv, block_n)
     if force_nsplit > 0:
         nsplit = min(force_nsplit, n_tiles)
     else:
         want = _cdiv(target_blocks_per_cu * n_cu, n_units)
-        nsplit = max(1, min(want, n_tiles, nsplit_cap))
+        nsplit = max(1, min(want, n_tiles, nsplit_cap, _cdiv(n_tiles, min_chunk_tiles)))
     chunk_tiles = _cdiv(n_tiles, nsplit)
     nsplit = _cdiv(n_tiles, chunk_tiles)
     return dict(nsplit=nsplit, chunk_tiles=chunk_tiles,

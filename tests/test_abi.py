@@ -54,7 +54,8 @@ def test_describe_equals_oracle_rule(B, S, Hq, Hkv, n_cu):
     _lib()
     info = V.describe_plan(B, 1, S, Hq, Hkv, 128, 0, n_cu_override=n_cu)
     units = Hkv * info["head_blocks"]
-    want = choose_decode_split(B, S, units, n_cu, info["block_n"])
+    want = choose_decode_split(B, S, units, n_cu, info["block_n"], target_blocks_per_cu=8,
+                               min_chunk_tiles=16)
     for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
         assert info[key] == int(want[key]), key
     # the default s_max grid follows the oracle's grid rule; the scheduled

@@ -64,8 +64,9 @@ def _w(name, B, Hq, Hkv, D, kv_lens, s_max_kv=None, B_max=None, causal=False, cu
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_tiny_decode_default_plan(seed):
+    # 128 keys at most: below the work floor of one split, so a direct pass
     r = run_decode(I.tiny_decode(seed), seed)
-    assert r["info"]["nsplit"] == 2 and not r["info"]["direct"]
+    assert r["info"]["nsplit"] == 1 and r["info"]["direct"]
     assert r["err_word"] == 0
 
 
@@ -118,8 +119,15 @@ def test_long_decode_full_size():
 
 
 def test_batched_decode_full_size():
+    # 512 (sequence, kv head) units at 8 workgroups per CU: 4 splits, MFMA path
     r = run_decode(I.batched_decode_step(0), 0)
-    assert r["info"]["direct"]
+    assert r["info"]["nsplit"] == 4 and r["info"]["decode_path"] == 2
+
+
+def test_batched_decode_full_size_direct_wave():
+    # the single-pass direct write on the wave path, at the same size
+    r = run_decode(I.batched_decode_step(1), 1, force_nsplit=1, force_decode_path=1)
+    assert r["info"]["direct"] and r["info"]["decode_path"] == 1
 
 
 @pytest.mark.parametrize("D", [32, 64, 256])

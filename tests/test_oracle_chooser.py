@@ -68,3 +68,22 @@ def test_prefill_grid():
     g = choose_prefill_grid(16, 4096, 8, 32)
     assert g["grid"] == 16 * 128 * 8
     assert choose_prefill_grid(3, 33, 2, 32)["n_qtiles"] == 2
+
+
+def test_work_floor_per_split():
+    # with at least 16 tiles per split: 2048 keys, 128 units -> 2 splits of 1024
+    p = choose_decode_split(16, 2048, 8, 256, 64, target_blocks_per_cu=8, min_chunk_tiles=16)
+    assert (p["nsplit"], p["chunk_keys"]) == (2, 1024)
+    # 8192 keys, 512 units at 8 per CU -> 4 splits (the floor allows 8)
+    p = choose_decode_split(64, 8192, 8, 256, 64, target_blocks_per_cu=8, min_chunk_tiles=16)
+    assert (p["nsplit"], p["chunk_keys"]) == (4, 2048)
+    # 128 keys: one split, direct write
+    assert choose_decode_split(2, 128, 1, 256, 64, target_blocks_per_cu=8,
+                               min_chunk_tiles=16)["direct"]
+    # the floor never lowers a count below what the tile count allows
+    for S in (1, 64, 1000, 5000, 32768):
+        for m in (1, 4, 16):
+            p = choose_decode_split(1, S, 1, 256, 64, target_blocks_per_cu=8, min_chunk_tiles=m)
+            n_tiles = -(-S // 64)
+            assert 1 <= p["nsplit"] <= max(1, -(-n_tiles // m))
+            assert p["chunk_tiles"] * p["nsplit"] >= n_tiles

@@ -14,7 +14,14 @@
 // ceil(target * n_cu / n_units) with n_units the decode workgroups per split;
 // "tile count" is ceil(s_max_kv / 64); splits are contiguous chunks of whole
 // tiles and the count is recomputed from the chunk size so that no split is
-// empty at s_max_kv.
+// empty at s_max_kv. The target itself is tuned for this chip: 8 workgroups
+// per CU measured best (a CU holds several decode workgroups at once, and
+// finer splits even out batches whose lengths vary, where the longest
+// sequence's workgroup would otherwise set the step time); the rule's form,
+// caps and direct-write fallback are unchanged. One bound is added: a split
+// keeps at least 16 tiles (1024 keys) at s_max_kv, below which the
+// per-workgroup start and merge cost more than the parallelism returns
+// (measured on 2048-key gathered lists and 8192-key batches).
 #include "plan.hpp"
 
 #include <stdint.h>
@@ -34,7 +41,7 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
   if (D != 32 && D != 64 && D != 128 && D != 256) return VATTN_ERR_UNSUPPORTED;
   vattn_plan_opts o = {};
   if (opts) o = *opts;
-  const int target = o.target_blocks_per_cu > 0 ? o.target_blocks_per_cu : 2;
+  const int target = o.target_blocks_per_cu > 0 ? o.target_blocks_per_cu : kDecodeTargetPerCu;
   const int cap = o.nsplit_cap > 0 ? o.nsplit_cap : 32;
   const int G = Hq / Hkv;
 
@@ -69,6 +76,9 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
       int64_t ns = want;
       if (ns > in.n_tiles) ns = in.n_tiles;
       if (ns > cap) ns = cap;
+      // each split keeps at least kMinChunkTiles tiles of work at s_max_kv
+      const int64_t by_work = cdiv(in.n_tiles, kMinChunkTiles);
+      if (ns > by_work) ns = by_work;
       nsplit = ns < 1 ? 1 : (int)ns;
     }
     const int chunk_tiles = cdiv(in.n_tiles, nsplit);

@@ -9,7 +9,10 @@ namespace vattn {
 constexpr int kDecodeBlockN = 64;     // decode KV tile used by the split rule (keys)
 constexpr int kDecodeMfmaHeads = 16;  // heads per workgroup on the MFMA decode path
 constexpr int kDecodeWaveHeads = 4;   // heads per workgroup on the wave decode path
-constexpr int kWaveMaxG = 4;          // auto: G <= this uses the wave path
+constexpr int kWaveMaxG = 3;          // auto: G <= this uses the wave path (MFMA measured
+                                      // faster from G = 4 on)
+constexpr int kDecodeTargetPerCu = 8;  // split rule: workgroups per CU to aim for
+constexpr int kMinChunkTiles = 16;     // split rule: fewest KV tiles per split
 // query rows (heads x tokens) per prefill workgroup: 8 waves (4 for D = 256)
 // of 32 rows; threads per prefill workgroup
 constexpr int prefill_rows(int D) { return D <= 128 ? 256 : 128; }

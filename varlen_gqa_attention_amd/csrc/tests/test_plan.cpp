@@ -30,9 +30,22 @@ int main() {
     CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, &fu, 256, &in) == VATTN_OK);
     CHECK(in.fused_combine == 1 && in.combine_grid == 0 && in.nsplit == 32);
   }
-  // batch * kv heads fills the device: direct write
+  // continuous batching: 512 units, 8 workgroups per CU -> 4 splits; G = 4 on the MFMA path
   CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
-  CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0 && in.decode_path == VATTN_DECODE_WAVE);
+  CHECK(!in.direct && in.nsplit == 4 && in.combine_grid == 64 * 32);
+  CHECK(in.decode_path == VATTN_DECODE_MFMA && in.threads == 256);
+  // 2048-key lists, 128 units: the work floor (16 tiles per split) gives 2 splits
+  CHECK(vattn::plan_compute(16, 1, 2048, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.nsplit == 2 && in.chunk_keys == 1024);
+  // tiny decode (128 keys): one split, direct write
+  CHECK(vattn::plan_compute(2, 1, 128, 4, 1, 64, 0, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.direct && in.nsplit == 1);
+  // batch * kv heads fills the device (8 workgroups per CU): direct write
+  CHECK(vattn::plan_compute(256, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0);
+  // small groups take the wave path
+  CHECK(vattn::plan_compute(64, 1, 8192, 16, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
+  CHECK(in.decode_path == VATTN_DECODE_WAVE);
   // prefill: G heads folded into 256 rows (D <= 128); default grid from
   // B_max and s_max_q
   CHECK(vattn::plan_compute(16, 4096, 4096, 32, 8, 128, 1, nullptr, 256, &in) == VATTN_OK);
@@ -66,10 +79,11 @@ int main() {
           CHECK(vattn::plan_compute(B, 1, S, Hkv * G, Hkv, 64, 0, nullptr, 256, &in) == VATTN_OK);
           const int tiles = cdiv(S, 64);
           CHECK(in.nsplit >= 1 && in.nsplit <= 32 && in.nsplit <= tiles);
+          CHECK(in.nsplit <= cdiv(tiles, 16));  // at least 16 tiles of work per split
           CHECK((in.nsplit - 1) * in.chunk_keys < tiles * 64 && in.nsplit * in.chunk_keys >= S);
           CHECK(in.grid == in.n_units * in.nsplit);
           CHECK(in.direct == (in.nsplit == 1));
-          if (in.n_units >= 512) CHECK(in.direct);
+          if (in.n_units >= 8 * 256) CHECK(in.direct);
         }
   vattn_plan_opts o = {};
   o.force_nsplit = 7;
