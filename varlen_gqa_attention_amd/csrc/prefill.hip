@@ -111,23 +111,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
     }
   }
 
-  // Q must be in registers before the loop: an explicit wait here tells the
-  // compiler's counter tracking so, and the loop's MFMAs then never wait on
-  // the tile prefetches issued inside the loop.
-  wait_vmem_all();
-
-  float m[RB], l[RB];
-  f32x16 o[RB][DBLK];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = kNegInf;
-    l[rb] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) o[rb][i][j] = 0.f;
-  }
-
   const int64_t krs = a.k_rs, vrs = a.v_rs;
   const uint16_t* kbase = a.k + (int64_t)sk.start * krs + hk * D;
   const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + hk * D;
@@ -163,10 +146,26 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
     }
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+  // Tile 0's loads share the Q loads' round trip. Q must be in registers
+  // before the loop: an explicit wait here tells the compiler's counter
+  // tracking so, and the loop's MFMAs then never wait on the tile prefetches
+  // issued inside the loop.
+  if (ntiles > 0) load_tile(0);
+  wait_vmem_all();
+
+  float m[RB], l[RB];
+  f32x16 o[RB][DBLK];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[rb][i][j] = 0.f;
   }
+
+  if (ntiles > 0) store_tile(0);
   if (ntiles > 1) load_tile(1);
 
   // The two halves of tile jt: h1 = S^T = K Q^T + online softmax (leaves
