@@ -30,6 +30,8 @@ Sources (web pages), cited in the modules by the short tags below:
 Modules:
   attention  fp64 varlen GQA attention, split partials and the LSE merge,
              attention over gathered (index-listed) keys
+  backward   fp64 gradients dq, dk, dv of the same attention (chain rule
+             through the softmax)
   brute      scalar pure-Python triple loops (tiny inputs only; a pin)
   mask       padding mask: vectorised formula and the per-sequence loop form
   chooser    plan-time split-count / grid rule
