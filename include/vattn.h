@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define VATTN_ABI_VERSION 2
+#define VATTN_ABI_VERSION 3
 
 typedef void* vattn_stream_t; /* a hipStream_t */
 
@@ -100,6 +100,9 @@ typedef struct {
   int prefill_grid;         /* prefill: 0 = grid sized from B_max and s_max_q whose
                                workgroups exit on dead tiles (default); 1 = device-built
                                schedule of live tiles on a persistent grid */
+  int backward;             /* 1: also size the plan for vattn_backward (allocates the
+                               row-wise <dO, O> buffer, B_max * s_max_q * Hq floats);
+                               D in {32, 64, 128} and G <= 128 only */
 } vattn_plan_opts;
 
 typedef struct {
@@ -121,6 +124,10 @@ typedef struct {
   int n_qtiles;        /* prefill: ceil(s_max_q / q_tokens_per_tile) */
   int threads;         /* threads per workgroup of the main kernel */
   int prefill_persistent; /* prefill: 1 = schedule kernel + persistent grid of `grid` */
+  int backward;        /* 1 if the plan serves vattn_backward */
+  int bwd_q_tokens_per_tile; /* backward dq kernel: query tokens per workgroup (128 / G) */
+  int bwd_grid_dq;     /* backward: workgroups of the dq kernel */
+  int bwd_grid_dkdv;   /* backward: workgroups of the dk/dv kernel (128 keys each) */
   long long scratch_bytes; /* device bytes owned by the plan */
 } vattn_plan_info;
 
@@ -222,6 +229,41 @@ vattn_status vattn_execute_strided(vattn_plan_t p, int B,
                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                                    void* out, int64_t out_row_stride, float* lse,
                                    int64_t q_rows, int64_t kv_rows, vattn_stream_t stream);
+
+/*
+ * Backward of the attention (cudnn-frontend issue #552, Related: THD backward
+ * engines under the forward's contract — packed or row-strided views, lengths
+ * read on the device, no host round trip). Given q, k, v, the forward's out
+ * and lse for the same plan, and the output gradient dout ([T_q, Hq, D]
+ * bf16), writes the gradients of sum(dout * out):
+ *   dq [T_q, Hq, D], dk, dv [T_kv, Hkv, D], bf16 (fp32 accumulation),
+ * with dk, dv summed over the G query heads of each KV head. With
+ * p_ij = exp(s_ij - lse_i): dv_j = sum_i p_ij dout_i; ds_ij = p_ij
+ * (<dout_i, v_j> - <dout_i, out_i>); dq_i = scale sum_j ds_ij k_j;
+ * dk_j = scale sum_i ds_ij q_i, over the visible pairs (same causal rule).
+ * Rows of dq of every sequence are written (0 for a row without visible
+ * keys); rows of dk, dv of every sequence are written (0 for keys no query
+ * sees); rows outside all sequences are not touched. Sequences must not share
+ * K/V rows. Strides as vattn_execute_strided (0 = packed; >= H * D and a
+ * multiple of 8; q_rs applies to q, out_rs to out, dout_rs to dout, and so
+ * on); q_rows bounds q, out, dout, lse and dq, kv_rows bounds k, v, dk and dv.
+ * Needs a plan made with opts.backward = 1 (VATTN_ERR_UNSUPPORTED otherwise).
+ * Enqueues two kernels (dq, which also stores <dout_i, out_i> in the plan's
+ * scratch, then dk/dv) and returns: no allocation, no synchronisation, no
+ * host read, so it can be captured. Deterministic: no atomics.
+ */
+vattn_status vattn_backward(vattn_plan_t p, int B,
+                            const void* q, int64_t q_row_stride,
+                            const void* k, int64_t k_row_stride,
+                            const void* v, int64_t v_row_stride,
+                            const void* out, int64_t out_row_stride,
+                            const void* dout, int64_t dout_row_stride,
+                            const float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                            void* dq, int64_t dq_row_stride,
+                            void* dk, int64_t dk_row_stride,
+                            void* dv, int64_t dv_row_stride,
+                            int64_t q_rows, int64_t kv_rows, vattn_stream_t stream);
 
 /*
  * Prefill comparator that the grid-sizing question asks to be measured

@@ -5,11 +5,24 @@ oracle, widened to one bf16 ulp of the reference where that is larger (from
 |O| >= 2, where the ulp is 2^-6; only very short KV reaches such values); fp32 LSE within 1e-3 relative
 (|d| <= 1e-3 * max(1, |LSE|), since LSE can sit near 0); -inf must match
 exactly and NaN always fails.
+
+Gradients (bf16 dq, dk, dv) against the unrounded fp64 oracle: every element
+within 2e-2 + 2^-8 |ref|, and the whole tensor within 1e-2 relative in the
+Frobenius norm. Derivation: the kernels round the softmax weights and dS to
+bf16 as MFMA operands (2^-9 relative each, random), take <dO, O> from the
+forward's bf16 output, and round the results to bf16 (the 2^-8 |ref| term);
+an emulation of exactly these roundings in fp64 (causal, L up to 2000, D 32
+and 128, N(0,1) inputs) gives element errors beyond the output rounding of at
+most 0.0094 and Frobenius ratios of 0.0021-0.0025, so both bounds hold a
+margin of 2x and 4x.
 """
 import numpy as np
 
 OUT_ATOL = 1e-2
 LSE_RTOL = 1e-3
+GRAD_ATOL = 2e-2
+GRAD_RTOL = 2.0 ** -8
+GRAD_FRO = 1e-2
 
 
 def bf16_ulp(x):
@@ -45,4 +58,25 @@ def assert_lse_close(got, ref, what=""):
     tol = LSE_RTOL * np.maximum(1.0, np.abs(r))
     bad = err > tol
     assert not bad.any(), f"{what}: {bad.sum()} LSE values out of tolerance, max err {err.max():.3e}"
+    return float(err.max()) if err.size else 0.0
+
+
+def assert_grad_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert not np.isnan(got).any(), f"{what}: NaN in gradient"
+    err = np.abs(got - ref)
+    bad = err > GRAD_ATOL + GRAD_RTOL * np.abs(ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} gradients out of tolerance; max err "
+                             f"{err.max():.3e}; first at {idx.tolist()} got "
+                             f"{[got[tuple(i)] for i in idx]} ref {[ref[tuple(i)] for i in idx]}")
+    nr = np.linalg.norm(ref)
+    if nr > 0:
+        fro = np.linalg.norm(got - ref) / nr
+        assert fro <= GRAD_FRO, f"{what}: relative Frobenius error {fro:.3e}"
+    else:
+        assert np.linalg.norm(got) == 0, f"{what}: nonzero gradient where the oracle has none"
     return float(err.max()) if err.size else 0.0

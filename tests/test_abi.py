@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (vattn_\w+)", out))
     assert set(declared_functions()) <= exported
-    assert L.vattn_abi_version() == 2
+    assert L.vattn_abi_version() == 3
 
 
 SWEEP = [(B, S, Hq, Hkv) for B in (1, 2, 33, 64, 300) for S in (1, 100, 4096, 32768)
@@ -98,3 +98,32 @@ def test_pure_cpp_plan_test(tmp_path):
                    check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D", [(1, 100, 8, 8, 64), (16, 4096, 32, 8, 128),
+                                          (3, 1000, 12, 4, 32), (64, 1, 128, 1, 128)])
+def test_describe_backward_grids(B, S, Hq, Hkv, D):
+    """Backward plans: the dq grid follows the forward's grid rule at 128 rows
+    per workgroup, the dk/dv grid covers 128-key tiles, and the plan's scratch
+    grows by the row-wise <dout, out> buffer."""
+    import varlen_gqa_attention_amd as V
+    _lib()
+    base = V.describe_plan(B, S, S, Hq, Hkv, D, 1, n_cu_override=256)
+    d = V.describe_plan(B, S, S, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
+    G = Hq // Hkv
+    g = choose_prefill_grid(B, S, Hkv, 128 // G)
+    assert d["backward"] == 1 and d["bwd_q_tokens_per_tile"] == 128 // G
+    assert d["bwd_grid_dq"] == 8 * -(-(B * Hkv) // 8) * g["n_qtiles"]
+    assert d["bwd_grid_dkdv"] == 8 * -(-(B * Hkv) // 8) * -(-S // 128)
+    assert d["scratch_bytes"] == base["scratch_bytes"] + 256 + 4 * B * S * Hq
+    assert base["backward"] == 0 and base["bwd_grid_dq"] == 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 256), (256, 1, 64)])
+def test_backward_plan_limits(Hq, Hkv, D):
+    import varlen_gqa_attention_amd as V
+    _lib()
+    with pytest.raises(V.VattnError) as e:
+        V.describe_plan(2, 64, 64, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
+    assert e.value.status == -2
+    V.describe_plan(2, 64, 64, Hq, Hkv, D, 1, n_cu_override=256)   # forward is fine

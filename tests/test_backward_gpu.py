@@ -1,0 +1,157 @@
+"""Backward (dq, dk, dv) through the C ABI vs the fp64 oracle (GPU).
+
+The forward runs on the GPU (its out and lse feed the backward, as in
+training); the oracle differentiates the exact attention of the same bf16
+inputs. Covers ragged packs with empty sequences, Lq != Lk both ways, a
+sequence without keys, several tiles per sequence, trailing cu entries past
+B, row-strided views, determinism and the error statuses.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import backward as BW
+from tests.parity import assert_grad_close
+from varlen_gqa_attention_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x4B80
+
+
+def _setup(q_lens, kv_lens, Hq, Hkv, D, seed, lead=3, tail=(-1, 2**31 - 1)):
+    B = len(q_lens)
+    cu_q = I.cu_from_lengths(q_lens, capacity=B + 1 + len(tail), tail=tail, start=lead)
+    cu_k = I.cu_from_lengths(kv_lens, capacity=B + 1 + len(tail), tail=tail, start=lead + 1)
+    Tq = lead + int(np.sum(q_lens)) + 2
+    Tk = lead + 1 + int(np.sum(kv_lens)) + 2
+    q = I.normal_bf16((Tq, Hq, D), 10 + seed, "cuda")
+    k = I.normal_bf16((Tk, Hkv, D), 20 + seed, "cuda")
+    v = I.normal_bf16((Tk, Hkv, D), 30 + seed, "cuda")
+    dout = I.normal_bf16((Tq, Hq, D), 40 + seed, "cuda")
+    return B, cu_q, cu_k, q, k, v, dout
+
+
+def _run(plan, B, cu_q, cu_k, q, k, v, dout):
+    cq, ck = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    out, lse = plan(q, k, v, cq, ck, B=B)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    for t in (dq, dk, dv):
+        t.view(torch.int16).fill_(SENT)
+    plan.backward(q, k, v, out, lse, dout, cq, ck, dq=dq, dk=dk, dv=dv, B=B)
+    torch.cuda.synchronize()
+    return out, lse, dq, dk, dv
+
+
+def _check(B, cu_q, cu_k, q, k, v, dout, dq, dk, dv, causal, what):
+    rq, rk, rv, wq, wk = BW.attend_varlen_backward(
+        I.bf16_to_f64(q), I.bf16_to_f64(k), I.bf16_to_f64(v), I.bf16_to_f64(dout), cu_q, cu_k,
+        B, causal)
+    assert_grad_close(I.bf16_to_f64(dq)[wq], rq[wq], what + " dq")
+    assert_grad_close(I.bf16_to_f64(dk)[wk], rk[wk], what + " dk")
+    assert_grad_close(I.bf16_to_f64(dv)[wk], rv[wk], what + " dv")
+    # rows that belong to no sequence are not written
+    for t, w in ((dq, wq), (dk, wk), (dv, wk)):
+        raw = t.view(torch.int16).cpu().numpy()
+        assert (raw[~w] == SENT).all()
+
+
+# lengths: an empty query side, Lq < Lk, Lq > Lk, a sequence without keys,
+# single tokens and tile boundaries +- 1
+Q_LENS = [70, 1, 0, 129, 200, 33, 4, 64]
+K_LENS = [70, 1, 5, 129, 250, 20, 0, 65]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_backward_matches_oracle(D, G, causal):
+    import varlen_gqa_attention_amd as V
+    Hkv = 2
+    Hq = Hkv * G
+    print(f"[backward] D={D} G={G} causal={causal}", flush=True)
+    B, cu_q, cu_k, q, k, v, dout = _setup(Q_LENS, K_LENS, Hq, Hkv, D, D + G)
+    plan = V.Plan(B + 2, 256, 256, Hq, Hkv, D, causal, backward=True)
+    _, _, dq, dk, dv = _run(plan, B, cu_q, cu_k, q, k, v, dout)
+    assert plan.read_error() == 0
+    _check(B, cu_q, cu_k, q, k, v, dout, dq, dk, dv, causal, f"D={D} G={G}")
+
+
+@pytest.mark.parametrize("G,D", [(8, 128), (2, 64), (16, 128)])
+def test_backward_several_tiles_per_sequence(G, D):
+    """Sequences spanning several query tiles, key tiles and 64-row steps."""
+    import varlen_gqa_attention_amd as V
+    Hkv = 1 if G == 16 else 2
+    Hq = Hkv * G
+    q_lens, kv_lens = [700, 300, 1025], [700, 513, 1025]
+    print(f"[backward] long G={G} D={D}", flush=True)
+    B, cu_q, cu_k, q, k, v, dout = _setup(q_lens, kv_lens, Hq, Hkv, D, 7 + G)
+    plan = V.Plan(B, 1100, 1100, Hq, Hkv, D, True, backward=True)
+    _, _, dq, dk, dv = _run(plan, B, cu_q, cu_k, q, k, v, dout)
+    _check(B, cu_q, cu_k, q, k, v, dout, dq, dk, dv, True, f"long G={G} D={D}")
+
+
+def test_backward_is_deterministic():
+    import varlen_gqa_attention_amd as V
+    B, cu_q, cu_k, q, k, v, dout = _setup([300, 77], [300, 90], 16, 2, 128, 3)
+    plan = V.Plan(B, 300, 300, 16, 2, 128, True, backward=True)
+    r1 = _run(plan, B, cu_q, cu_k, q, k, v, dout)
+    r2 = _run(plan, B, cu_q, cu_k, q, k, v, dout)
+    for a, b in zip(r1[2:], r2[2:]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_backward_on_fused_buffers_equals_packed_bitwise():
+    """q/k/v as slices of one fused QKV buffer and dq/dk/dv as slices of one
+    fused gradient buffer: bit-identical to packed copies, other bytes of the
+    fused gradient buffer untouched."""
+    import varlen_gqa_attention_amd as V
+    Hq, Hkv, D = 8, 2, 64
+    lens = [90, 1, 200]
+    cu = I.cu_from_lengths(lens)
+    T = int(cu[-1])
+    qkv = I.normal_bf16((T, Hq + 2 * Hkv, D), 5, "cuda")
+    q, k, v = qkv[:, :Hq], qkv[:, Hq:Hq + Hkv], qkv[:, Hq + Hkv:]
+    dout = I.normal_bf16((T, Hq, D), 6, "cuda")
+    cq = torch.from_numpy(cu).cuda()
+    plan = V.Plan(3, 256, 256, Hq, Hkv, D, True, backward=True)
+    out, lse = plan(q.contiguous(), k.contiguous(), v.contiguous(), cq, cq)
+    dq0, dk0, dv0 = plan.backward(q.contiguous(), k.contiguous(), v.contiguous(), out, lse, dout,
+                                  cq, cq)
+    g = torch.empty(T, Hq + 2 * Hkv + 1, D, dtype=torch.bfloat16, device="cuda")
+    g.view(torch.int16).fill_(SENT)
+    dq, dk, dv = g[:, :Hq], g[:, Hq:Hq + Hkv], g[:, Hq + Hkv:Hq + 2 * Hkv]
+    plan.backward(q, k, v, out, lse, dout, cq, cq, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq0), (dk, dk0), (dv, dv0)):
+        assert torch.equal(a.contiguous().view(torch.int16), b.view(torch.int16))
+    assert bool((g[:, Hq + 2 * Hkv:].view(torch.int16) == SENT).all())
+
+
+def test_backward_needs_a_backward_plan_and_valid_strides():
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import _lib
+    L = _lib.load()
+    Hq, Hkv, D = 4, 2, 64
+    q = torch.zeros(8, Hq, D, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(8, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(8, Hq, device="cuda")
+    cu = torch.tensor([0, 8], dtype=torch.int32, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    plain = V.Plan(1, 8, 8, Hq, Hkv, D, True)
+    with pytest.raises(V.VattnError) as e:
+        plain.backward(q, k, k, q, lse, q, cu, cu)
+    assert e.value.status == -2
+    plan = V.Plan(1, 8, 8, Hq, Hkv, D, True, backward=True)
+
+    def call(q_rs, dk_rs):
+        return L.vattn_backward(plan._h, 1, P(q), q_rs, P(k), 0, P(k), 0, P(q), 0, P(q), 0,
+                                P(lse), P(cu), P(cu), P(q), 0, P(k), dk_rs, P(k), 0, 8, 8, None)
+    assert call(Hq * D - 8, 0) == -1         # rows would overlap
+    assert call(0, Hkv * D + 4) == -1        # not 16-byte aligned
+    assert call(0, 0) == 0
+    torch.cuda.synchronize()

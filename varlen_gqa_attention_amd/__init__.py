@@ -34,9 +34,9 @@ __all__ = ["Plan", "padding_mask", "cross_padding_masks", "describe_plan", "Vatt
 
 
 def _opts(target_blocks_per_cu=0, nsplit_cap=0, force_nsplit=0, force_decode_path=0,
-          n_cu_override=0, fuse_combine=0, decode_waves=0, prefill_grid=0):
+          n_cu_override=0, fuse_combine=0, decode_waves=0, prefill_grid=0, backward=0):
     return PlanOpts(target_blocks_per_cu, nsplit_cap, force_nsplit, force_decode_path,
-                    n_cu_override, fuse_combine, decode_waves, prefill_grid)
+                    n_cu_override, fuse_combine, decode_waves, prefill_grid, int(backward))
 
 
 def describe_plan(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, **opts):
@@ -147,6 +147,36 @@ class Plan:
             _ptr(kv_idx), _ptr(out), _ptr(lse), q.shape[0], k.shape[0], kv_idx.numel(),
             _stream_of(q, stream)), "vattn_execute_gathered")
         return out, lse
+
+    def backward(self, q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_kv, dq=None, dk=None,
+                 dv=None, B=None, stream=None):
+        """Gradients (dq, dk, dv) of sum(dout * out) for a plan made with
+        backward=True; out and lse are this plan's forward results. Tensors
+        may be token-row-strided views (heads and head dims contiguous)."""
+        import torch
+        if dq is None:
+            dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+        if dk is None:
+            dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+        if dv is None:
+            dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+        if B is None:
+            B = cu_seqlens_q.numel() - 1
+        if cu_seqlens_q.numel() < B + 1 or cu_seqlens_kv.numel() < B + 1:
+            raise ValueError("cu_seqlens buffers need at least B + 1 entries")
+        self._check(q, k, v, cu_seqlens_q, cu_seqlens_kv, out, lse, row_strided=True)
+        for name, t, like in (("dout", dout, q), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or t.shape != like.shape:
+                raise ValueError(f"{name} must be a bf16 device tensor shaped like {tuple(like.shape)}")
+            if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+                raise ValueError(f"{name}: heads and head dims must be contiguous")
+        _lib.check(_LIB.vattn_backward(
+            self._h, B, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+            _ptr(out), out.stride(0), _ptr(dout), dout.stride(0), _ptr(lse),
+            _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(dq), dq.stride(0), _ptr(dk),
+            dk.stride(0), _ptr(dv), dv.stride(0), q.shape[0], k.shape[0],
+            _stream_of(q, stream)), "vattn_backward")
+        return dq, dk, dv
 
     def execute_exact_grid(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, tile_map, out, lse, B,
                            stream=None):

@@ -24,7 +24,7 @@ ERRBIT_Q_LEN, ERRBIT_KV_LEN, ERRBIT_ROWS, ERRBIT_INDEX = 0x1, 0x2, 0x4, 0x8
 EXPORTS = (
     "vattn_status_string", "vattn_abi_version", "vattn_plan", "vattn_plan_ex",
     "vattn_plan_describe", "vattn_plan_query", "vattn_execute", "vattn_execute_gathered",
-    "vattn_execute_strided",
+    "vattn_execute_strided", "vattn_backward",
     "vattn_execute_exact_grid", "vattn_padding_mask", "vattn_cross_padding_mask",
     "vattn_plan_error_word",
     "vattn_plan_read_error", "vattn_plan_clear_error", "vattn_plan_set_kernel_events",
@@ -35,14 +35,15 @@ EXPORTS = (
 class PlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "target_blocks_per_cu", "nsplit_cap", "force_nsplit", "force_decode_path",
-        "n_cu_override", "fuse_combine", "decode_waves", "prefill_grid")]
+        "n_cu_override", "fuse_combine", "decode_waves", "prefill_grid", "backward")]
 
 
 _INFO_INT_FIELDS = (
     "B_max", "s_max_q", "s_max_kv", "Hq", "Hkv", "D", "causal", "is_decode", "decode_path",
     "n_cu", "block_n", "n_tiles", "nsplit", "chunk_keys", "direct", "fused_combine",
     "head_blocks", "n_units", "grid", "combine_grid", "q_tokens_per_tile", "n_qtiles",
-    "threads", "prefill_persistent")
+    "threads", "prefill_persistent", "backward", "bwd_q_tokens_per_tile", "bwd_grid_dq",
+    "bwd_grid_dkdv")
 
 
 class PlanInfo(ctypes.Structure):
@@ -95,6 +96,9 @@ def load():
     L.vattn_execute_strided.restype = c_int
     L.vattn_execute_strided.argtypes = [vp, c_int, vp, c_i64, vp, c_i64, vp, c_i64, vp, vp, vp,
                                         c_i64, vp, c_i64, c_i64, vp]
+    L.vattn_backward.restype = c_int
+    L.vattn_backward.argtypes = [vp, c_int] + [vp, c_i64] * 5 + [vp, vp, vp] + [vp, c_i64] * 3 + \
+        [c_i64, c_i64, vp]
     L.vattn_execute_exact_grid.restype = c_int
     L.vattn_execute_exact_grid.argtypes = [vp, c_int, vp, vp, vp, vp, vp, vp, vp, c_i64, c_i64,
                                            vp, c_int, vp]

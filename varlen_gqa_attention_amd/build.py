@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "decode.hip", "prefill.hip", "mask.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "decode.hip", "prefill.hip", "mask.hip", "bwd.hip"]
 ARCH = os.environ.get("VATTN_OFFLOAD_ARCH", "gfx950")
 
 

@@ -23,6 +23,7 @@ struct vattn_plan_s {
   float* part_o;
   int32_t* sched_count;  // prefill schedule: live-tile count, then the list
   int32_t* sched_list;
+  float* delta;          // backward: [B_max, s_max_q, Hq] row-wise <dout, out>
   hipEvent_t ev_start, ev_stop;  // measurement hook (caller-owned), or null
 };
 
@@ -98,6 +99,9 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   uintptr_t total = off_o + n_part * (uintptr_t)D * sizeof(float);
   if (info.prefill_persistent)
     total = 512 + (uintptr_t)B_max * info.n_qtiles * sizeof(int32_t);
+  // backward: the row-wise <dout, out> buffer at the end
+  const uintptr_t off_delta = align_up(total, 256);
+  if (info.backward) total = off_delta + (uintptr_t)B_max * s_max_q * Hq * sizeof(float);
   p->info.scratch_bytes = (long long)total;
   void* mem = nullptr;
   hipError_t e = hipMalloc(&mem, total);
@@ -113,6 +117,7 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   p->part_o = n_part ? (float*)(p->scratch + off_o) : nullptr;
   p->sched_count = info.prefill_persistent ? (int32_t*)(p->scratch + 256) : nullptr;
   p->sched_list = info.prefill_persistent ? (int32_t*)(p->scratch + 512) : nullptr;
+  p->delta = info.backward ? (float*)(p->scratch + off_delta) : nullptr;
   // plan creation may synchronise (it is not on the hot path): zero the
   // error word once with a kernel, then wait for it.
   if (vattn::launch_clear_word(p->err, nullptr) != hipSuccess ||
@@ -327,6 +332,82 @@ vattn_status vattn_execute_exact_grid(vattn_plan_t p, int B, const void* q, cons
   if (B == 0 || n_tiles == 0) return VATTN_OK;
   return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, tile_map, n_tiles,
              packed_strides(p->info), stream);
+}
+
+vattn_status vattn_backward(vattn_plan_t p, int B, const void* q, int64_t q_row_stride,
+                            const void* k, int64_t k_row_stride, const void* v,
+                            int64_t v_row_stride, const void* out, int64_t out_row_stride,
+                            const void* dout, int64_t dout_row_stride, const float* lse,
+                            const int32_t* cu_q, const int32_t* cu_kv, void* dq,
+                            int64_t dq_row_stride, void* dk, int64_t dk_row_stride, void* dv,
+                            int64_t dv_row_stride, int64_t q_rows, int64_t kv_rows,
+                            vattn_stream_t stream) {
+  if (!p) return VATTN_ERR_INVALID_ARG;
+  if (!p->info.backward) return VATTN_ERR_UNSUPPORTED;
+  vattn_status st =
+      check_exec(p, B, q, k, v, cu_q, cu_kv, const_cast<void*>(out), const_cast<float*>(lse),
+                 q_rows, kv_rows);
+  if (st != VATTN_OK) return st;
+  const vattn_plan_info& in = p->info;
+  const int64_t pq = (int64_t)in.Hq * in.D, pk = (int64_t)in.Hkv * in.D;
+  const int64_t rs[8] = {q_row_stride,   k_row_stride,  v_row_stride,  out_row_stride,
+                         dout_row_stride, dq_row_stride, dk_row_stride, dv_row_stride};
+  const int64_t packed[8] = {pq, pk, pk, pq, pq, pq, pk, pk};
+  int64_t r[8];
+  for (int i = 0; i < 8; ++i) {
+    r[i] = rs[i] ? rs[i] : packed[i];
+    if (r[i] < packed[i] || (r[i] & 7)) return VATTN_ERR_INVALID_ARG;
+  }
+  if (B == 0) return VATTN_OK;
+  if (!dout || !dq || !dk || !dv) return VATTN_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return VATTN_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  if (p->ev_start) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(hs, &cs) != hipSuccess) return VATTN_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return VATTN_ERR_INVALID_ARG;
+  }
+  vattn::BwdArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.out = (const uint16_t*)out;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.cu_q = cu_q;
+  a.cu_kv = cu_kv;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.delta = p->delta;
+  a.err = p->err;
+  a.B = B;
+  a.B_max = in.B_max;
+  a.Hq = in.Hq;
+  a.Hkv = in.Hkv;
+  a.G = in.Hq / in.Hkv;
+  a.tq = in.bwd_q_tokens_per_tile;
+  a.n_qtiles = (in.s_max_q + a.tq - 1) / a.tq;
+  a.n_ktiles = (in.s_max_kv + vattn::kBwdKeys - 1) / vattn::kBwdKeys;
+  a.s_max_q = in.s_max_q;
+  a.s_max_kv = in.s_max_kv;
+  a.q_rows = q_rows;
+  a.kv_rows = kv_rows;
+  a.q_rs = r[0];
+  a.k_rs = r[1];
+  a.v_rs = r[2];
+  a.o_rs = r[3];
+  a.do_rs = r[4];
+  a.dq_rs = r[5];
+  a.dk_rs = r[6];
+  a.dv_rs = r[7];
+  a.scale = (float)(1.0 / std::sqrt((double)in.D));
+  a.c = (float)(1.0 / std::sqrt((double)in.D) * 1.4426950408889634);
+  a.causal = in.causal;
+  hipError_t e = vattn::launch_backward(a, in.D, in.bwd_grid_dq, in.bwd_grid_dkdv, hs,
+                                        p->ev_start, p->ev_stop);
+  return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
 }
 
 vattn_status vattn_padding_mask(const int32_t* cu_seqlens, int B, int max_seqlen, uint8_t* mask,

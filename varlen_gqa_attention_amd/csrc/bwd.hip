@@ -1,0 +1,480 @@
+// Backward of causal varlen GQA attention on gfx950: dq, dk, dv (bf16) from
+// q, k, v, the forward's out and lse, and the output gradient dout.
+//
+// The pages name a THD backward under the forward's contract (cudnn-frontend
+// issue #552, Related: the THD backward contract): packed or row-strided
+// views, device-read cu_seqlens, dead tiles exiting, no host round trip. The
+// arithmetic is the derivative of the forward through the softmax, with the
+// softmax weights recomputed from the stored log-sum-exp:
+//   p_ij = exp(s_ij - LSE_i), dp_ij = <dO_i, v_j>, delta_i = <dO_i, O_i>,
+//   ds_ij = p_ij (dp_ij - delta_i), dq_i = scale sum_j ds_ij k_j,
+//   dk_j = scale sum_i ds_ij q_i, dv_j = sum_i p_ij dO_i
+// (dk, dv summed over the G query heads that read KV head j's head).
+//
+// Two kernels, no atomics (results do not depend on scheduling):
+//  * dq kernel: workgroup = (sequence, KV head, query tile) with the G heads
+//    folded into 128 rows, as in the forward. Per 64-key tile: S^T = K Q^T
+//    and dP^T = V dO^T (Q^T and dO^T in registers, K and V rows from LDS),
+//    P and dS in registers (one row per lane), dQ^T += K^T dS^T with K^T from
+//    the transposed LDS read. Its prologue also computes delta_i from dO and
+//    O and stores it for the second kernel.
+//  * dk/dv kernel: workgroup = (sequence, KV head, 128-key tile), 32 keys per
+//    wave with K and V of those keys in registers. It walks the query rows
+//    that can see its keys (64 tokens of one query head per step, all G
+//    heads): S = Q K^T and dP = dO V^T with Q and dO rows from LDS, P and dS
+//    (one key per lane), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and
+//    Q^T from the transposed LDS read.
+// Every contraction is v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
+// dS are rounded to bf16 as MFMA operands. Tiles reach a two-stage LDS ring
+// through registers (loads two steps ahead, one barrier per step).
+#include <hip/hip_ext.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace vattn {
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+__device__ __forceinline__ bf16x4 bwd_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
+
+__device__ __forceinline__ void bwd_wait_vmem() {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+}
+
+template <int D>
+struct BwdCfg {
+  static constexpr int NW = 4;                 // waves per workgroup (one per SIMD)
+  static constexpr int THREADS = NW * 64;
+  static constexpr int BN = 64;                // keys (dq) or query rows (dk/dv) per step
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int KS = D / 16;            // k-steps of 16 over d
+  static constexpr int DBLK = D / 32;          // 32-wide d blocks
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int CH = (BN * CPR + THREADS - 1) / THREADS;  // 16-byte chunks per thread
+};
+
+// A-operand fragment of a 32-row block of a row-major LDS tile (rows of D
+// bf16, swz_rows layout): lane holds row 32 blk + lane % 32, elements
+// 16 ks + 8 (lane / 32) .. + 8.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows(const uint8_t* t, int blk, int ks, int lane) {
+  const int r = 32 * blk + (lane & 31);
+  const int c = 2 * ks + (lane >> 5);
+  return __builtin_bit_cast(bf16x8,
+                            *reinterpret_cast<const u32x4*>(t + r * D * 2 + swz_rows<D>(r, c) * 16));
+}
+
+// A-operand fragment of the transpose of a 64-row LDS tile (swz_rows layout)
+// for k-step `step` (16 rows) and d block db: lane holds column
+// d = 32 db + lane % 32 at the 8 rows that the bf16 packing of a 32x32 MFMA
+// accumulator (see pack_acc) puts in lane / 32's half of that k-step.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr(const uint8_t* t, int step, int db, int lane) {
+  const int g = lane >> 4, m16 = lane & 15;
+  const int blk = step >> 1, h = step & 1;
+  const int r1 = 32 * blk + 16 * h + 4 * (g >> 1) + (m16 >> 2);
+  const int r2 = r1 + 8;
+  const int col = 32 * db + 16 * (g & 1) + 4 * (m16 & 3);
+  const int ch = col >> 3, half = (col >> 2) & 1;
+  const bf16x4 x1 = bwd_read_tr(t + r1 * D * 2 + swz_rows<D>(r1, ch) * 16 + half * 8);
+  const bf16x4 x2 = bwd_read_tr(t + r2 * D * 2 + swz_rows<D>(r2, ch) * 16 + half * 8);
+  return __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// bf16 B operand for k-step (blk, h) from a 32x32 accumulator block: lane
+// holds accumulator entries 8 h .. 8 h + 7 (rows 16 h + 4 (lane / 32) + 0..3
+// and + 8..11 of the block).
+__device__ __forceinline__ bf16x8 pack_acc(const f32x16& x, int h) {
+  u32x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(x[8 * h + 2 * j], x[8 * h + 2 * j + 1]);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s = fmaf(bf16_lo(a[j]), bf16_lo(b[j]), s);
+    s = fmaf(bf16_hi(a[j]), bf16_hi(b[j]), s);
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// dq kernel (also writes delta)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * C::TILE_BYTES];
+
+  const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
+  const int u = x + 8 * (p / a.n_qtiles);
+  if (u >= a.B_max * a.Hkv) return;
+  const int b = u / a.Hkv, hk = u % a.Hkv, qt = a.n_qtiles - 1 - p % a.n_qtiles;
+  if (b >= a.B) return;
+  const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
+  const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
+  if (qt == 0 && hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
+  const int Lq = sq.len, Lk = sk.len;
+  const int t0 = qt * a.tq;
+  if (t0 >= Lq) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int shift = Lk - Lq;
+  const int t_last = min(t0 + a.tq - 1, Lq - 1);
+  const int kend = a.causal ? max(0, min(Lk, t_last + shift + 1)) : Lk;
+  const int kfull = a.causal ? max(0, min(Lk, t0 + shift + 1)) : Lk;
+
+  const int row = 32 * w + (lane & 31);
+  const int hl = row / a.tq;
+  const int tok = t0 + row % a.tq;
+  const bool row_ok = hl < a.G && tok < Lq;
+  const int hq = hk * a.G + hl;
+  const int row_lim = a.causal ? tok + shift : Lk - 1;
+  const int64_t qrow = (int64_t)sq.start + tok;
+
+  // Q^T, dO^T operands and O (for delta): lane holds row's elements
+  // 16 ks + 8 (lane / 32) .. + 8
+  bf16x8 qv[KS], dov[KS];
+  float delta = 0.f, lse = kNegInf;
+  {
+    const int off = hq * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 xq = {0, 0, 0, 0}, xd = {0, 0, 0, 0}, xo = {0, 0, 0, 0};
+      if (row_ok) {
+        xq = ld16(a.q + qrow * a.q_rs + off + 16 * ks);
+        xd = ld16(a.dout + qrow * a.do_rs + off + 16 * ks);
+        xo = ld16(a.out + qrow * a.o_rs + off + 16 * ks);
+      }
+      qv[ks] = __builtin_bit_cast(bf16x8, xq);
+      dov[ks] = __builtin_bit_cast(bf16x8, xd);
+      delta += dot8(xd, xo);
+    }
+    if (row_ok) lse = a.lse[qrow * a.Hq + hq];
+  }
+
+  const int64_t krs = a.k_rs, vrs = a.v_rs;
+  const uint16_t* kbase = a.k + (int64_t)sk.start * krs + hk * D;
+  const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + hk * D;
+  const int ntiles = (kend + BN - 1) / BN;
+  u32x4 stk[CH], stv[CH];
+  auto load_tile = [&](int jt) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      const int r = q / CPR, c = q % CPR;
+      const int64_t key = min(jt * BN + r, kend - 1);
+      stk[i] = ld16(kbase + key * krs + 8 * c);
+      stv[i] = ld16(vbase + key * vrs + 8 * c);
+    }
+  };
+  auto store_tile = [&](int jt) {
+    uint8_t* sk_ = lds + (jt & 1) * 2 * C::TILE_BYTES;
+    uint8_t* sv_ = sk_ + C::TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      const int r = q / CPR, c = q % CPR;
+      *reinterpret_cast<u32x4*>(sk_ + r * D * 2 + swz_rows<D>(r, c) * 16) = stk[i];
+      *reinterpret_cast<u32x4*>(sv_ + r * D * 2 + swz_rows<D>(r, c) * 16) = stv[i];
+    }
+  };
+  if (ntiles > 0) load_tile(0);
+  bwd_wait_vmem();
+
+  delta = sum_xor32(delta);
+  if (row_ok && lane < 32) a.delta[((int64_t)b * a.s_max_q + tok) * a.Hq + hq] = delta;
+  // exponent offset in base 2; a row without visible keys (lse = -inf) gets
+  // +inf so that every weight is exp2(-inf) = 0
+  const float lse2 = (lse == kNegInf) ? __builtin_inff() : lse * kLog2e;
+
+  f32x16 dq[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dq[i][j] = 0.f;
+
+  if (ntiles > 0) store_tile(0);
+  if (ntiles > 1) load_tile(1);
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    __syncthreads();
+    if (jt + 1 < ntiles) {
+      store_tile(jt + 1);
+      if (jt + 2 < ntiles) load_tile(jt + 2);
+    }
+    const uint8_t* lk = lds + (jt & 1) * 2 * C::TILE_BYTES;
+    const uint8_t* lv = lk + C::TILE_BYTES;
+    const int key0 = jt * BN;
+    // S^T = K Q^T and dP^T = V dO^T, two 32-key blocks
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(lk, kb, ks, lane), qv[ks],
+                                                        s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(lv, kb, ks, lane), dov[ks],
+                                                         dp[kb], 0, 0, 0);
+      }
+    // P and dS (lane: one row; keys key0 + 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
+    const bool need_mask = key0 + BN > kfull;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(fmaf(s[kb][i], a.c, -lse2));
+        if (need_mask) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (key > row_lim || key >= Lk) pv = 0.f;
+        }
+        s[kb][i] = pv * (dp[kb][i] - delta);
+      }
+    // dQ^T += K^T dS^T over four 16-key k-steps
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      const bf16x8 bds = pack_acc(s[step >> 1], step & 1);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(lk, step, db, lane), bds,
+                                                         dq[db], 0, 0, 0);
+    }
+  }
+
+  // epilogue: lane holds dQ^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][row]
+  if (!row_ok) return;
+  uint16_t* op = a.dq + qrow * a.dq_rs + hq * D + 4 * (lane >> 5);
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      u32x2 wv;
+      wv[0] = pack_bf16x2(dq[db][4 * i4 + 0] * a.scale, dq[db][4 * i4 + 1] * a.scale);
+      wv[1] = pack_bf16x2(dq[db][4 * i4 + 2] * a.scale, dq[db][4 * i4 + 3] * a.scale);
+      *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i4) = wv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk / dv kernel
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = BwdCfg<D>;
+  constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
+  constexpr int KEYS = 32 * C::NW;                  // keys per workgroup
+  constexpr int STAGE = 2 * C::TILE_BYTES + 2 * BN * 4;  // Q, dO tiles + lse2, delta rows
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+
+  const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
+  const int u = x + 8 * (p / a.n_ktiles);
+  if (u >= a.B_max * a.Hkv) return;
+  const int b = u / a.Hkv, hk = u % a.Hkv, kt = p % a.n_ktiles;
+  if (b >= a.B) return;
+  const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
+  const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
+  const int Lq = sq.len, Lk = sk.len;
+  const int j0 = kt * KEYS;
+  if (j0 >= Lk) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int shift = Lk - Lq;
+  const int key = j0 + 32 * w + (lane & 31);
+  const bool key_ok = key < Lk;
+  const int64_t krow = (int64_t)sk.start + key;
+
+  // K^T, V^T operands: lane holds key's elements 16 ks + 8 (lane / 32) .. + 8
+  bf16x8 kv_[KS], vv[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 xk = {0, 0, 0, 0}, xv = {0, 0, 0, 0};
+    if (key_ok) {
+      xk = ld16(a.k + krow * a.k_rs + hk * D + 8 * (lane >> 5) + 16 * ks);
+      xv = ld16(a.v + krow * a.v_rs + hk * D + 8 * (lane >> 5) + 16 * ks);
+    }
+    kv_[ks] = __builtin_bit_cast(bf16x8, xk);
+    vv[ks] = __builtin_bit_cast(bf16x8, xv);
+  }
+
+  // query rows that can see a key of this tile: tokens from t_first (causal:
+  // key j0 needs token >= j0 - shift), 64 tokens of one query head per step
+  const int t_first = a.causal ? max(0, j0 - shift) : 0;
+  const int n_tb = Lq > t_first ? (Lq - t_first + BN - 1) / BN : 0;
+  const int n_it = n_tb * a.G;
+
+  u32x4 stq[CH], std_[CH];
+  float st_lse = 0.f, st_dl = 0.f;
+  auto load_step = [&](int it) {
+    const int tb = it / a.G, hq = hk * a.G + it % a.G;
+    const int tbase = t_first + tb * BN;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      const int r = q / CPR, c = q % CPR;
+      const int64_t t = sq.start + min(tbase + r, Lq - 1);
+      stq[i] = ld16(a.q + t * a.q_rs + hq * D + 8 * c);
+      std_[i] = ld16(a.dout + t * a.do_rs + hq * D + 8 * c);
+    }
+    if (threadIdx.x < BN) {
+      const int tk = tbase + threadIdx.x;
+      const int tc = min(tk, Lq - 1);
+      const float ls = a.lse[((int64_t)sq.start + tc) * a.Hq + hq];
+      // rows past the sequence, or without visible keys, get weight 0
+      st_lse = (tk >= Lq || ls == kNegInf) ? __builtin_inff() : ls * kLog2e;
+      st_dl = a.delta[((int64_t)b * a.s_max_q + tc) * a.Hq + hq];
+    }
+  };
+  auto store_step = [&](int it) {
+    uint8_t* s0 = lds + (it & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      const int r = q / CPR, c = q % CPR;
+      *reinterpret_cast<u32x4*>(s0 + r * D * 2 + swz_rows<D>(r, c) * 16) = stq[i];
+      *reinterpret_cast<u32x4*>(s0 + C::TILE_BYTES + r * D * 2 + swz_rows<D>(r, c) * 16) =
+          std_[i];
+    }
+    if (threadIdx.x < BN) {
+      float* rows = reinterpret_cast<float*>(s0 + 2 * C::TILE_BYTES);
+      rows[threadIdx.x] = st_lse;
+      rows[BN + threadIdx.x] = st_dl;
+    }
+  };
+  if (n_it > 0) load_step(0);
+  bwd_wait_vmem();
+
+  f32x16 dk[DBLK], dv[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dk[i][j] = dv[i][j] = 0.f;
+
+  if (n_it > 0) store_step(0);
+  if (n_it > 1) load_step(1);
+
+  for (int it = 0; it < n_it; ++it) {
+    __syncthreads();
+    if (it + 1 < n_it) {
+      store_step(it + 1);
+      if (it + 2 < n_it) load_step(it + 2);
+    }
+    const uint8_t* lq = lds + (it & 1) * STAGE;
+    const uint8_t* ldo = lq + C::TILE_BYTES;
+    const float* lrow = reinterpret_cast<const float*>(lq + 2 * C::TILE_BYTES);
+    const int tbase = t_first + (it / a.G) * BN;
+    // S = Q K^T and dP = dO V^T for two 32-row blocks
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[rb][j] = dp[rb][j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(lq, rb, ks, lane), kv_[ks],
+                                                        s[rb], 0, 0, 0);
+        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(ldo, rb, ks, lane), vv[ks],
+                                                         dp[rb], 0, 0, 0);
+      }
+    // P and dS (lane: one key; rows 32 rb + 8 g + 4 (lane/32) + 0..3)
+    // visible iff key < Lk and (not causal or key <= token + shift); rows
+    // past the sequence carry lse2 = +inf
+    f32x16 pp[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = 32 * rb + 8 * g + 4 * (lane >> 5);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lrow + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(lrow + BN + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          float pv = fast_exp2(fmaf(s[rb][i], a.c, -l4[e]));
+          const bool vis = key_ok && (!a.causal || key <= tbase + r0 + e + shift);
+          pv = vis ? pv : 0.f;
+          pp[rb][i] = pv;
+          s[rb][i] = pv * (dp[rb][i] - d4[e]);
+        }
+      }
+    // dV^T += dO^T P and dK^T += Q^T dS over four 16-row k-steps
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      const bf16x8 bp = pack_acc(pp[step >> 1], step & 1);
+      const bf16x8 bds = pack_acc(s[step >> 1], step & 1);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(ldo, step, db, lane), bp,
+                                                         dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(lq, step, db, lane), bds,
+                                                         dk[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue: lane holds dK^T / dV^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][key]
+  if (!key_ok) return;
+  uint16_t* kp = a.dk + krow * a.dk_rs + hk * D + 4 * (lane >> 5);
+  uint16_t* vp = a.dv + krow * a.dv_rs + hk * D + 4 * (lane >> 5);
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2(dk[db][4 * i4 + 0] * a.scale, dk[db][4 * i4 + 1] * a.scale);
+      wk[1] = pack_bf16x2(dk[db][4 * i4 + 2] * a.scale, dk[db][4 * i4 + 3] * a.scale);
+      wv[0] = pack_bf16x2(dv[db][4 * i4 + 0], dv[db][4 * i4 + 1]);
+      wv[1] = pack_bf16x2(dv[db][4 * i4 + 2], dv[db][4 * i4 + 3]);
+      *reinterpret_cast<u32x2*>(kp + 32 * db + 8 * i4) = wk;
+      *reinterpret_cast<u32x2*>(vp + 32 * db + 8 * i4) = wv;
+    }
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, int grid_dq, int grid_dkdv, hipStream_t st,
+                               hipEvent_t ev0, hipEvent_t ev1) {
+  using C = BwdCfg<D>;
+  // with measurement events, ev0 is stamped at the dq kernel's start and ev1
+  // at the dk/dv kernel's end (the whole backward)
+  if (ev0)
+    hipExtLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(C::THREADS), 0, st, ev0, nullptr,
+                          0, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(C::THREADS), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev0)
+    hipExtLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid_dkdv), dim3(C::THREADS), 0, st, nullptr,
+                          ev1, 0, a);
+  else
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(grid_dkdv), dim3(C::THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs& a, int D, int grid_dq, int grid_dkdv, hipStream_t st,
+                           hipEvent_t ev0, hipEvent_t ev1) {
+  switch (D) {
+    case 32: return launch_bwd_d<32>(a, grid_dq, grid_dkdv, st, ev0, ev1);
+    case 64: return launch_bwd_d<64>(a, grid_dq, grid_dkdv, st, ev0, ev1);
+    case 128: return launch_bwd_d<128>(a, grid_dq, grid_dkdv, st, ev0, ev1);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vattn

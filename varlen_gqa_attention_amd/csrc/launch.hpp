@@ -59,6 +59,33 @@ struct PrefillArgs {
   int causal;
 };
 
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;  // [B_max, s_max_q, Hq] row-wise <dO, O>, written by the dq kernel
+  int32_t* err;
+  int B, B_max, Hq, Hkv, G;
+  int tq;        // dq kernel: query tokens per workgroup (rows = G * tq = 128)
+  int n_qtiles;  // ceil(s_max_q / tq)
+  int n_ktiles;  // dk/dv kernel: ceil(s_max_kv / 128)
+  int s_max_q, s_max_kv;
+  int64_t q_rows, kv_rows;
+  // row (token) strides in elements
+  int64_t q_rs, k_rs, v_rs, o_rs, do_rs, dq_rs, dk_rs, dv_rs;
+  float c;       // scale * log2(e)
+  float scale;
+  int causal;
+};
+
 // ev0 / ev1 (may be null): measurement events stamped with the start / end
 // of the split (or direct) kernel's dispatch; the combine kernel is not timed.
 hipError_t launch_decode(const DecodeArgs& a, int path, int nw, int grid, int combine_grid,
@@ -76,5 +103,10 @@ hipError_t launch_cross_padding_mask(const int32_t* cu_q, const int32_t* cu_kv, 
                                      int max_q, int max_kv, uint8_t* mask_q, uint8_t* mask_kv,
                                      hipStream_t st);
 hipError_t launch_clear_word(int32_t* word, hipStream_t st);
+// dq kernel (grid_dq workgroups) then dk/dv kernel (grid_dkdv), both > 0;
+// ev0 / ev1 (may be null) are stamped at the start of the first and the end
+// of the second.
+hipError_t launch_backward(const BwdArgs& a, int D, int grid_dq, int grid_dkdv, hipStream_t st,
+                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 }  // namespace vattn

@@ -68,7 +68,7 @@ template <int D>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds, int b, int hk,
                                              int qt) {
   using C = PrefillCfg<D>;
-  constexpr int NW = C::NW, RB = C::RB, BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK;
+  constexpr int RB = C::RB, BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK;
   constexpr int NSTAGE = C::NSTAGE;
   if (b < 0 || b >= a.B || qt >= a.n_qtiles) return;
   const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
