@@ -321,6 +321,48 @@ def prefill_measure(args, reps=10):
                 exact_grid_with_host_roundtrip_us=round(med(per_r) * 1e3, 1))
 
 
+def backward_measure(args, reps=10):
+    """Backward (dq, dk, dv) on the causal varlen prefill workload: the
+    forward's out and lse feed it, dout is seeded N(0, 1) bf16. Algorithmic
+    flop = 8 * Hq * D per visible pair (the four length-D products dv, dp, dq,
+    dk of each pair); the kernels also recompute S and dP in both passes."""
+    torch = _torch()
+    import numpy as np
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    w = I.varlen_prefill(0)
+    if getattr(args, "prefill_len", 0):
+        w["q_lens"] = w["kv_lens"] = np.full(w["B"], args.prefill_len, dtype=np.int64)
+        w["name"] += f" (all lengths {args.prefill_len})"
+    m = I.materialise(w, 0, "cuda")
+    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], True,
+                  backward=True)
+    out, lse = plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], B=w["B"])
+    dout = I.normal_bf16(tuple(m["q"].shape), 77, "cuda")
+    dq, dk, dv = torch.empty_like(m["q"]), torch.empty_like(m["k"]), torch.empty_like(m["v"])
+    pairs = visible_pairs(w["q_lens"], w["kv_lens"])
+    flop = 8 * w["Hq"] * w["D"] * pairs
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    f = lambda: plan.backward(m["q"], m["k"], m["v"], out, lse, dout, m["cu_q"], m["cu_kv"],
+                              dq=dq, dk=dk, dv=dv, B=w["B"])
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        f()
+        torch.cuda.synchronize()
+    _, per = time_replays([f], reps, 2)
+    ms = med(per)
+    kern = kernel_event_times(plan, [f], reps)
+    tfl = flop / (ms * 1e-3) / 1e12
+    return dict(workload=w["name"] + ": backward, B=16, L~U[64,4096] (seed 3,0), Hq=32, Hkv=8, "
+                         "D=128, s_max 4096",
+                flop=flop, flop_rule="8 * Hq * D per visible (query, key) pair",
+                us=round(ms * 1e3, 1), tflops=round(tfl, 1),
+                frac_mfma_peak=round(tfl / MFMA_BF16_PEAK_TFLOPS, 4),
+                kernels_us=round(med(kern) * 1e3, 1),
+                grids=dict(dq=plan.info["bwd_grid_dq"], dkdv=plan.info["bwd_grid_dkdv"]),
+                timing=f"median of {reps} eager calls (dq kernel + dk/dv kernel), HIP events")
+
+
 def batched_decode_measure(args, steps=100):
     torch = _torch()
     import numpy as np
@@ -456,7 +498,8 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=0,
                     help="long decode: steps per captured graph (0 = one per K/V copy)")
     ap.add_argument("--workload", default="long_decode",
-                    choices=["long_decode", "prefill", "batched_decode", "gathered_decode"],
+                    choices=["long_decode", "prefill", "batched_decode", "gathered_decode",
+                             "backward"],
                     help="headline workload (default: long decode); the others are for "
                          "profiling runs")
     args = ap.parse_args()
@@ -479,7 +522,8 @@ def main():
                           **gathered_measure(**{k: v for k, v in args.plan_opts.items() if v})}))
         return
     if args.workload != "long_decode":
-        fn = prefill_measure if args.workload == "prefill" else batched_decode_measure
+        fn = {"prefill": prefill_measure, "backward": backward_measure}.get(
+            args.workload, batched_decode_measure)
         print(json.dumps({"workload": args.workload, **fn(args)}))
         return
     res, state = long_decode(args)
@@ -492,6 +536,7 @@ def main():
         line["prefill"] = prefill_measure(args)
         line["batched_decode"] = batched_decode_measure(args)
         line["gathered_decode"] = gathered_measure()
+        line["backward"] = backward_measure(args)
         line["padding_mask"] = mask_measure()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)

@@ -111,6 +111,7 @@ template <int D>
 __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
   constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
+  constexpr int PF = KS < 2 ? KS : 2;  // k-steps of LDS reads in flight
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * C::TILE_BYTES];
 
   const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
@@ -221,15 +222,36 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dq_kernel(BwdArgs a
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    // K and V row fragments stream from LDS PF k-steps ahead of their MFMAs
+    // (the scheduling barriers keep the reads from sinking next to their use)
+    bf16x8 kf[2][KS], vf[2][KS];
+    auto rd = [&](int ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(lk, kb, ks, lane), qv[ks],
-                                                        s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(lv, kb, ks, lane), dov[ks],
-                                                         dp[kb], 0, 0, 0);
+        kf[kb][ks] = frag_rows<D>(lk, kb, ks, lane);
+        vf[kb][ks] = frag_rows<D>(lv, kb, ks, lane);
       }
+    };
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) rd(ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) rd(ks + PF);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qv[ks], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][ks], dov[ks], dp[kb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // first K^T fragments of the dQ product, read while the VALU works
+    bf16x8 kt[4][DBLK];
+    auto rdt = [&](int step) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) kt[step][db] = frag_tr<D>(lk, step, db, lane);
+    };
+    rdt(0);
     // P and dS (lane: one row; keys key0 + 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
     const bool need_mask = key0 + BN > kfull;
 #pragma unroll
@@ -243,14 +265,16 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dq_kernel(BwdArgs a
         }
         s[kb][i] = pv * (dp[kb][i] - delta);
       }
-    // dQ^T += K^T dS^T over four 16-key k-steps
+    // dQ^T += K^T dS^T over four 16-key k-steps, K^T read one step ahead
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
+      if (step + 1 < 4) rdt(step + 1);
       const bf16x8 bds = pack_acc(s[step >> 1], step & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(lk, step, db, lane), bds,
-                                                         dq[db], 0, 0, 0);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[step][db], bds, dq[db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -276,6 +300,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   using C = BwdCfg<D>;
   constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
   constexpr int KEYS = 32 * C::NW;                  // keys per workgroup
+  constexpr int PF = KS < 2 ? KS : 2;                // k-steps of LDS reads in flight
   constexpr int STAGE = 2 * C::TILE_BYTES + 2 * BN * 4;  // Q, dO tiles + lse2, delta rows
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
@@ -383,15 +408,38 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[rb][j] = dp[rb][j] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    // Q and dO row fragments stream from LDS PF k-steps ahead of their MFMAs
+    bf16x8 qf[2][KS], df[2][KS];
+    auto rd = [&](int ks) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(lq, rb, ks, lane), kv_[ks],
-                                                        s[rb], 0, 0, 0);
-        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(ldo, rb, ks, lane), vv[ks],
-                                                         dp[rb], 0, 0, 0);
+        qf[rb][ks] = frag_rows<D>(lq, rb, ks, lane);
+        df[rb][ks] = frag_rows<D>(ldo, rb, ks, lane);
       }
+    };
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) rd(ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) rd(ks + PF);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][ks], kv_[ks], s[rb], 0, 0, 0);
+        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[rb][ks], vv[ks], dp[rb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // first transposed fragments of the dV / dK products, read while the VALU works
+    bf16x8 dt[4][DBLK], qt[4][DBLK];
+    auto rdt = [&](int step) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        dt[step][db] = frag_tr<D>(ldo, step, db, lane);
+        qt[step][db] = frag_tr<D>(lq, step, db, lane);
+      }
+    };
+    rdt(0);
     // P and dS (lane: one key; rows 32 rb + 8 g + 4 (lane/32) + 0..3)
     // visible iff key < Lk and (not causal or key <= token + shift); rows
     // past the sequence carry lse2 = +inf
@@ -416,15 +464,16 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
     // dV^T += dO^T P and dK^T += Q^T dS over four 16-row k-steps
 #pragma unroll
     for (int step = 0; step < 4; ++step) {
+      if (step + 1 < 4) rdt(step + 1);
       const bf16x8 bp = pack_acc(pp[step >> 1], step & 1);
       const bf16x8 bds = pack_acc(s[step >> 1], step & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(ldo, step, db, lane), bp,
-                                                         dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(lq, step, db, lane), bds,
-                                                         dk[db], 0, 0, 0);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[step][db], bp, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[step][db], bds, dk[db], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
