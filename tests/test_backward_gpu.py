@@ -155,3 +155,42 @@ def test_backward_needs_a_backward_plan_and_valid_strides():
     assert call(0, Hkv * D + 4) == -1        # not 16-byte aligned
     assert call(0, 0) == 0
     torch.cuda.synchronize()
+
+
+def test_backward_full_size_varlen_prefill_sampled():
+    """The benchmark's backward workload at full size (B=16, L~U[64,4096],
+    Hq=32, Hkv=8, D=128, plan s_max 4096, the same launch configuration):
+    for the longest and the shortest sequence and one KV head, every dq row
+    of the G query heads and every dk / dv row against the oracle's per-head
+    gradients, summed over the group."""
+    import varlen_gqa_attention_amd as V
+    w = I.varlen_prefill(0)
+    m = I.materialise(w, 0, "cuda")
+    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], True,
+                  backward=True)
+    out, lse = plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], B=w["B"])
+    dout = I.normal_bf16(tuple(m["q"].shape), 77, "cuda")
+    dq, dk, dv = plan.backward(m["q"], m["k"], m["v"], out, lse, dout, m["cu_q"], m["cu_kv"],
+                               B=w["B"])
+    torch.cuda.synchronize()
+    G = w["Hq"] // w["Hkv"]
+    scale = 1.0 / np.sqrt(w["D"])
+    lens = np.asarray(w["q_lens"])
+    for b in (int(np.argmax(lens)), int(np.argmin(lens))):
+        hk = 3
+        q0, L = int(m["cu_q_np"][b]), int(lens[b])
+        print(f"[backward full size] sequence {b} length {L} kv head {hk}", flush=True)
+        sl = slice(q0, q0 + L)
+        kh = I.bf16_to_f64(m["k"][sl, hk])
+        vh = I.bf16_to_f64(m["v"][sl, hk])
+        vis = np.tril(np.ones((L, L), dtype=bool))
+        rk = np.zeros((L, w["D"]))
+        rv = np.zeros((L, w["D"]))
+        for h in range(hk * G, hk * G + G):
+            gq, gk, gv = BW.backward_rows(I.bf16_to_f64(m["q"][sl, h]), kh, vh,
+                                          I.bf16_to_f64(dout[sl, h]), vis, scale)
+            assert_grad_close(I.bf16_to_f64(dq[sl, h]), gq, f"dq b={b} h={h}")
+            rk += gk
+            rv += gv
+        assert_grad_close(I.bf16_to_f64(dk[sl, hk]), rk, f"dk b={b}")
+        assert_grad_close(I.bf16_to_f64(dv[sl, hk]), rv, f"dv b={b}")
