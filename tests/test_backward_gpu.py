@@ -194,3 +194,83 @@ def test_backward_full_size_varlen_prefill_sampled():
             rv += gv
         assert_grad_close(I.bf16_to_f64(dk[sl, hk]), rk, f"dk b={b}")
         assert_grad_close(I.bf16_to_f64(dv[sl, hk]), rv, f"dv b={b}")
+
+
+def test_backward_graph_replay_with_changing_lengths():
+    """Forward + backward captured once in a graph and replayed with new
+    device-side lengths (copied into the captured cu buffers between replays
+    by the program's own eager work): every replay equals the eager call on
+    the same lengths, bit for bit."""
+    import varlen_gqa_attention_amd as V
+    Hq, Hkv, D, smax, B = 8, 2, 64, 300, 4
+    steps = 4
+    lens = [I.uniform_lengths(B, 0, smax, 9, t) for t in range(steps)]
+    T = smax * B
+    q = I.normal_bf16((T, Hq, D), 1, "cuda")
+    k = I.normal_bf16((T, Hkv, D), 2, "cuda")
+    v = I.normal_bf16((T, Hkv, D), 3, "cuda")
+    dout = I.normal_bf16((T, Hq, D), 4, "cuda")
+    plan = V.Plan(B, smax, smax, Hq, Hkv, D, True, backward=True)
+    cu = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    out = torch.zeros_like(q)
+    lse = torch.zeros(T, Hq, device="cuda")
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+
+    def step():
+        plan(q, k, v, cu, cu, out=out, lse=lse, B=B)
+        plan.backward(q, k, v, out, lse, dout, cu, cu, dq=dq, dk=dk, dv=dv, B=B)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="global"):
+        step()
+    torch.cuda.synchronize()
+    for t in range(steps):
+        cu.copy_(torch.from_numpy(I.cu_from_lengths(lens[t])).cuda())
+        for x in (dq, dk, dv):
+            x.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in (dq, dk, dv)]
+        for x in (dq, dk, dv):
+            x.zero_()
+        step()                                    # eager, same lengths
+        torch.cuda.synchronize()
+        for a, b in zip(got, (dq, dk, dv)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), t
+
+
+def test_backward_clamps_and_flags_invalid_lengths_and_b0_is_a_noop():
+    """A length above s_max is clamped (as in the forward) and flagged; the
+    gradients equal the oracle's on the clamped sequence. B = 0 enqueues
+    nothing."""
+    import varlen_gqa_attention_amd as V
+    Hq, Hkv, D = 4, 1, 64
+    plan = V.Plan(2, 96, 96, Hq, Hkv, D, True, backward=True)
+    q = I.normal_bf16((200, Hq, D), 11, "cuda")
+    k = I.normal_bf16((200, Hkv, D), 12, "cuda")
+    v = I.normal_bf16((200, Hkv, D), 13, "cuda")
+    dout = I.normal_bf16((200, Hq, D), 14, "cuda")
+    cu = np.array([0, 150, 190], dtype=np.int32)          # first length 150 > s_max 96
+    cu_t = torch.from_numpy(cu).cuda()
+    out, lse = plan(q, k, v, cu_t, cu_t, B=2)
+    plan.clear_error()
+    dq, dk, dv = (torch.zeros_like(x) for x in (q, k, v))
+    plan.backward(q, k, v, out, lse, dout, cu_t, cu_t, dq=dq, dk=dk, dv=dv, B=2)
+    torch.cuda.synchronize()
+    assert plan.read_error() & V.ERRBIT_Q_LEN
+    rq, rk, rv, wq, wk = BW.attend_varlen_backward(
+        I.bf16_to_f64(q), I.bf16_to_f64(k), I.bf16_to_f64(v), I.bf16_to_f64(dout), cu, cu, 2,
+        True, s_max_q=96, s_max_kv=96)
+    assert_grad_close(I.bf16_to_f64(dq)[wq], rq[wq], "clamped dq")
+    assert_grad_close(I.bf16_to_f64(dk)[wk], rk[wk], "clamped dk")
+    assert_grad_close(I.bf16_to_f64(dv)[wk], rv[wk], "clamped dv")
+    before = [x.clone() for x in (dq, dk, dv)]
+    plan.backward(q, k, v, out, lse, dout, cu_t, cu_t, dq=dq, dk=dk, dv=dv, B=0)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, (dq, dk, dv)))
