@@ -402,35 +402,28 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
     const uint8_t* ldo = lq + C::TILE_BYTES;
     const float* lrow = reinterpret_cast<const float*>(lq + 2 * C::TILE_BYTES);
     const int tbase = t_first + (it / a.G) * BN;
-    // S = Q K^T and dP = dO V^T for two 32-row blocks
-    f32x16 s[2], dp[2];
+    // Per step, two 32-row halves in a software pipeline, so that each
+    // half's softmax-gradient VALU work runs under the other half's MFMAs:
+    //   A: S, dP of rows 0-31
+    //   B: S, dP of rows 32-63      | P, dS of rows 0-31
+    //   C: dV, dK from rows 0-31    | P, dS of rows 32-63
+    //   D: dV, dK from rows 32-63
+    // (S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS). Fragment
+    // reads for a region are issued during the region before it.
+    f32x16 s[2], dp[2], pp[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s[rb][j] = dp[rb][j] = 0.f;
-    // Q and dO row fragments stream from LDS PF k-steps ahead of their MFMAs
     bf16x8 qf[2][KS], df[2][KS];
-    auto rd = [&](int ks) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        qf[rb][ks] = frag_rows<D>(lq, rb, ks, lane);
-        df[rb][ks] = frag_rows<D>(ldo, rb, ks, lane);
-      }
+    auto rd = [&](int rb, int ks) {
+      qf[rb][ks] = frag_rows<D>(lq, rb, ks, lane);
+      df[rb][ks] = frag_rows<D>(ldo, rb, ks, lane);
     };
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks) rd(ks);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) rd(ks + PF);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][ks], kv_[ks], s[rb], 0, 0, 0);
-        dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[rb][ks], vv[ks], dp[rb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // first transposed fragments of the dV / dK products, read while the VALU works
+    auto mm = [&](int rb, int ks) {
+      s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rb][ks], kv_[ks], s[rb], 0, 0, 0);
+      dp[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df[rb][ks], vv[ks], dp[rb], 0, 0, 0);
+    };
     bf16x8 dt[4][DBLK], qt[4][DBLK];
     auto rdt = [&](int step) {
 #pragma unroll
@@ -439,42 +432,86 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
         qt[step][db] = frag_tr<D>(lq, step, db, lane);
       }
     };
-    rdt(0);
-    // P and dS (lane: one key; rows 32 rb + 8 g + 4 (lane/32) + 0..3)
-    // visible iff key < Lk and (not causal or key <= token + shift); rows
-    // past the sequence carry lse2 = +inf
-    f32x16 pp[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r0 = 32 * rb + 8 * g + 4 * (lane >> 5);
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lrow + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(lrow + BN + r0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          float pv = fast_exp2(fmaf(s[rb][i], a.c, -l4[e]));
-          const bool vis = key_ok && (!a.causal || key <= tbase + r0 + e + shift);
-          pv = vis ? pv : 0.f;
-          pp[rb][i] = pv;
-          s[rb][i] = pv * (dp[rb][i] - d4[e]);
-        }
-      }
-    // dV^T += dO^T P and dK^T += Q^T dS over four 16-row k-steps
-#pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      if (step + 1 < 4) rdt(step + 1);
+    auto mmt = [&](int step) {
       const bf16x8 bp = pack_acc(pp[step >> 1], step & 1);
       const bf16x8 bds = pack_acc(s[step >> 1], step & 1);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[step][db], bp, dv[db], 0, 0, 0);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[step][db], bds, dk[db], 0, 0, 0);
       }
+    };
+    // P and dS of one half (lane: one key; rows 32 rb + 8 g + 4 (lane/32)
+    // + 0..3); visible iff key < Lk and (not causal or key <= token + shift);
+    // rows past the sequence carry lse2 = +inf. grad(rb, i0) does entries
+    // i0, i0 + 1 of the half, whose lse2 / delta were read into l4 / d4.
+    f32x4 l4[4], d4[4];
+    auto rows_of = [&](int rb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = 32 * rb + 8 * g + 4 * (lane >> 5);
+        l4[g] = *reinterpret_cast<const f32x4*>(lrow + r0);
+        d4[g] = *reinterpret_cast<const f32x4*>(lrow + BN + r0);
+      }
+    };
+    auto grad = [&](int rb, int i0) {
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i) {
+        const int g = i >> 2, e = i & 3;
+        const int row = 32 * rb + 8 * g + 4 * (lane >> 5) + e;
+        float pv = fast_exp2(fmaf(s[rb][i], a.c, -l4[g][e]));
+        const bool vis = key_ok && (!a.causal || key <= tbase + row + shift);
+        pv = vis ? pv : 0.f;
+        pp[rb][i] = pv;
+        s[rb][i] = pv * (dp[rb][i] - d4[g][e]);
+      }
+    };
+    // A
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) rd(0, ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) rd(0, ks + PF);
+      else rd(1, ks + PF - KS);
+      __builtin_amdgcn_sched_barrier(0);
+      mm(0, ks);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // B: two entries of rows 0-31 per k-step of rows 32-63 (the order of
+    // the source is kept by the scheduling barriers)
+    rows_of(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) rd(1, ks + PF);
+      if (ks == KS - 2) rdt(0);
+      if (ks == KS - 1) rdt(1);
+      mm(1, ks);
+#pragma unroll
+      for (int i0 = 16 * ks / KS; i0 < 16 * (ks + 1) / KS; i0 += 2) grad(0, i0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // C: two entries of rows 32-63 per d block of the rows 0-31 products
+    rows_of(1);
+#pragma unroll
+    for (int step = 0; step < 2; ++step) {
+      const bf16x8 bp = pack_acc(pp[0], step);
+      const bf16x8 bds = pack_acc(s[0], step);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        if (step == 1 && db == 0) rdt(2);
+        if (step == 1 && db == DBLK - 1) rdt(3);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[step][db], bp, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[step][db], bds, dk[db], 0, 0, 0);
+        const int j = step * DBLK + db;
+#pragma unroll
+        for (int i0 = 16 * j / (2 * DBLK); i0 < 16 * (j + 1) / (2 * DBLK); i0 += 2) grad(1, i0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // D
+    mmt(2);
+    mmt(3);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // epilogue: lane holds dK^T / dV^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][key]
