@@ -103,7 +103,7 @@ def test_pure_cpp_plan_test(tmp_path):
 @pytest.mark.parametrize("B,S,Hq,Hkv,D", [(1, 100, 8, 8, 64), (16, 4096, 32, 8, 128),
                                           (3, 1000, 12, 4, 32), (64, 1, 128, 1, 128)])
 def test_describe_backward_grids(B, S, Hq, Hkv, D):
-    """Backward plans: the dq grid follows the forward's grid rule at 128 rows
+    """Backward plans: the dq grid follows the forward's grid rule at 256 rows
     per workgroup, the dk/dv grid covers 128-key tiles, and the plan's scratch
     grows by the row-wise <dout, out> buffer."""
     import varlen_gqa_attention_amd as V
@@ -111,19 +111,20 @@ def test_describe_backward_grids(B, S, Hq, Hkv, D):
     base = V.describe_plan(B, S, S, Hq, Hkv, D, 1, n_cu_override=256)
     d = V.describe_plan(B, S, S, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
     G = Hq // Hkv
-    g = choose_prefill_grid(B, S, Hkv, 128 // G)
-    assert d["backward"] == 1 and d["bwd_q_tokens_per_tile"] == 128 // G
+    g = choose_prefill_grid(B, S, Hkv, 256 // G)
+    assert d["backward"] == 1 and d["bwd_q_tokens_per_tile"] == 256 // G
     assert d["bwd_grid_dq"] == 8 * -(-(B * Hkv) // 8) * g["n_qtiles"]
     assert d["bwd_grid_dkdv"] == 8 * -(-(B * Hkv) // 8) * -(-S // 128)
     assert d["scratch_bytes"] == base["scratch_bytes"] + 256 + 4 * B * S * Hq
     assert base["backward"] == 0 and base["bwd_grid_dq"] == 0
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 256), (256, 1, 64)])
-def test_backward_plan_limits(Hq, Hkv, D):
+@pytest.mark.parametrize("s_max_q,Hq,Hkv,D", [(64, 8, 2, 256), (1, 512, 1, 64)])
+def test_backward_plan_limits(s_max_q, Hq, Hkv, D):
+    """D = 256 and G > 256 have no backward; the forward plan is fine."""
     import varlen_gqa_attention_amd as V
     _lib()
     with pytest.raises(V.VattnError) as e:
-        V.describe_plan(2, 64, 64, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
+        V.describe_plan(2, s_max_q, 64, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
     assert e.value.status == -2
-    V.describe_plan(2, 64, 64, Hq, Hkv, D, 1, n_cu_override=256)   # forward is fine
+    V.describe_plan(2, s_max_q, 64, Hq, Hkv, D, 1, n_cu_override=256)

@@ -13,7 +13,8 @@
 //
 // Two kernels, no atomics (results do not depend on scheduling):
 //  * dq kernel: workgroup = (sequence, KV head, query tile) with the G heads
-//    folded into 128 rows, as in the forward. Per 64-key tile: S^T = K Q^T
+//    folded into 256 rows, 8 waves of 32 rows (two per SIMD), as in the
+//    forward. Per 64-key tile, one 32-key half after the other: S^T = K Q^T
 //    and dP^T = V dO^T (Q^T and dO^T in registers, K and V rows from LDS),
 //    P and dS in registers (one row per lane), dQ^T += K^T dS^T with K^T from
 //    the transposed LDS read. Its prologue also computes delta_i from dO and
@@ -44,9 +45,9 @@ __device__ __forceinline__ void bwd_wait_vmem() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 }
 
-template <int D>
+template <int D, int WAVES = 4>
 struct BwdCfg {
-  static constexpr int NW = 4;                 // waves per workgroup (one per SIMD)
+  static constexpr int NW = WAVES;             // waves per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int BN = 64;                // keys (dq) or query rows (dk/dv) per step
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
@@ -108,8 +109,8 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
 // dq kernel (also writes delta)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dq_kernel(BwdArgs a) {
-  using C = BwdCfg<D>;
+__global__ __launch_bounds__((BwdCfg<D, 8>::THREADS)) void bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D, 8>;  // 8 waves of 32 rows, two per SIMD
   constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
   constexpr int PF = KS < 2 ? KS : 2;  // k-steps of LDS reads in flight
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * C::TILE_BYTES];
@@ -216,65 +217,61 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dq_kernel(BwdArgs a
     const uint8_t* lk = lds + (jt & 1) * 2 * C::TILE_BYTES;
     const uint8_t* lv = lk + C::TILE_BYTES;
     const int key0 = jt * BN;
-    // S^T = K Q^T and dP^T = V dO^T, two 32-key blocks
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
-    // K and V row fragments stream from LDS PF k-steps ahead of their MFMAs
-    // (the scheduling barriers keep the reads from sinking next to their use)
-    bf16x8 kf[2][KS], vf[2][KS];
-    auto rd = [&](int ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        kf[kb][ks] = frag_rows<D>(lk, kb, ks, lane);
-        vf[kb][ks] = frag_rows<D>(lv, kb, ks, lane);
-      }
-    };
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks) rd(ks);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) rd(ks + PF);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb][ks], qv[ks], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][ks], dov[ks], dp[kb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // first K^T fragments of the dQ product, read while the VALU works
-    bf16x8 kt[4][DBLK];
-    auto rdt = [&](int step) {
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) kt[step][db] = frag_tr<D>(lk, step, db, lane);
-    };
-    rdt(0);
-    // P and dS (lane: one row; keys key0 + 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
     const bool need_mask = key0 + BN > kfull;
+    // the two 32-key halves one after the other (one S^T / dP^T block pair
+    // in registers at a time, which keeps a wave within the 256 registers of
+    // two waves per SIMD)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T; K and V row fragments stream from LDS
+      // PF k-steps ahead of their MFMAs (the scheduling barriers keep the
+      // reads from sinking next to their use)
+      f32x16 s, dp;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
+      bf16x8 kf[KS], vf[KS];
+      auto rd = [&](int ks) {
+        kf[ks] = frag_rows<D>(lk, kb, ks, lane);
+        vf[ks] = frag_rows<D>(lv, kb, ks, lane);
+      };
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) rd(ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) rd(ks + PF);
+        __builtin_amdgcn_sched_barrier(0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qv[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], dov[ks], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // K^T fragments of the half's two 16-key k-steps, read while the VALU works
+      bf16x8 kt[2][DBLK];
+      auto rdt = [&](int h) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) kt[h][db] = frag_tr<D>(lk, 2 * kb + h, db, lane);
+      };
+      rdt(0);
+      // P and dS (lane: one row; keys key0 + 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(fmaf(s[kb][i], a.c, -lse2));
+        float pv = fast_exp2(fmaf(s[i], a.c, -lse2));
         if (need_mask) {
           const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
           if (key > row_lim || key >= Lk) pv = 0.f;
         }
-        s[kb][i] = pv * (dp[kb][i] - delta);
+        s[i] = pv * (dp[i] - delta);
       }
-    // dQ^T += K^T dS^T over four 16-key k-steps, K^T read one step ahead
+      // dQ^T += K^T dS^T over the half's two k-steps, K^T read one step ahead
 #pragma unroll
-    for (int step = 0; step < 4; ++step) {
-      if (step + 1 < 4) rdt(step + 1);
-      const bf16x8 bds = pack_acc(s[step >> 1], step & 1);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int h = 0; h < 2; ++h) {
+        if (h == 0) rdt(1);
+        const bf16x8 bds = pack_acc(s, h);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[step][db], bds, dq[db], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < DBLK; ++db)
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[h][db], bds, dq[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -538,11 +535,12 @@ static hipError_t launch_bwd_d(const BwdArgs& a, int grid_dq, int grid_dkdv, hip
   using C = BwdCfg<D>;
   // with measurement events, ev0 is stamped at the dq kernel's start and ev1
   // at the dk/dv kernel's end (the whole backward)
+  constexpr int DQ_THREADS = BwdCfg<D, 8>::THREADS;
   if (ev0)
-    hipExtLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(C::THREADS), 0, st, ev0, nullptr,
+    hipExtLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(DQ_THREADS), 0, st, ev0, nullptr,
                           0, a);
   else
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(C::THREADS), 0, st, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(DQ_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev0)

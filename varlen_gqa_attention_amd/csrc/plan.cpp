@@ -136,7 +136,7 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     }
   }
   if (o.backward == 1) {
-    // backward kernels: dq workgroups of 128 rows (G heads folded), dk/dv
+    // backward kernels: dq workgroups of 256 rows (G heads folded), dk/dv
     // workgroups of 128 keys; the grids cover B_max x s_max like the forward
     if (D > 128 || G > kBwdRows) return VATTN_ERR_UNSUPPORTED;
     in.backward = 1;

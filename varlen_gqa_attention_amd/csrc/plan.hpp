@@ -17,9 +17,9 @@ constexpr int kMinChunkTiles = 16;     // split rule: fewest KV tiles per split
 // of 32 rows; threads per prefill workgroup
 constexpr int prefill_rows(int D) { return D <= 128 ? 256 : 128; }
 constexpr int prefill_threads(int D) { return D <= 128 ? 512 : 256; }
-// backward: query rows (heads x tokens) per dq workgroup and keys per dk/dv
-// workgroup (4 waves of 32 each)
-constexpr int kBwdRows = 128;
+// backward: query rows (heads x tokens) per dq workgroup (8 waves of 32) and
+// keys per dk/dv workgroup (4 waves of 32)
+constexpr int kBwdRows = 256;
 constexpr int kBwdKeys = 128;
 // largest query-tile count per sequence the on-device prefill schedule handles
 constexpr int kSchedMaxQtiles = 8192;
