@@ -530,8 +530,8 @@ def main():
                          "profiling runs")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 (sharding across GPUs is "
+                                   "not implemented)"}))
         sys.exit(2)
     args.plan_opts = dict(target_blocks_per_cu=args.target_blocks,
                           force_nsplit=args.force_nsplit, force_decode_path=args.decode_path,
