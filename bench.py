@@ -325,6 +325,18 @@ def prefill_measure(args, reps=10):
                                            out, lse, w["B"])
     _, per_e = time_replays([fe], reps, 2)
 
+    # declared strides: q, k, v as slices of one fused QKV buffer, out as a
+    # slice of a wider buffer (no copies; same kernel, strided addressing)
+    Tq = m["q"].shape[0]
+    qkv = torch.empty(Tq, w["Hq"] + 2 * w["Hkv"], w["D"], dtype=torch.bfloat16, device="cuda")
+    qkv[:, :w["Hq"]] = m["q"]
+    qkv[:, w["Hq"]:w["Hq"] + w["Hkv"]] = m["k"]
+    qkv[:, w["Hq"] + w["Hkv"]:] = m["v"]
+    wide = torch.empty(Tq, w["Hq"] + 8, w["D"], dtype=torch.bfloat16, device="cuda")
+    qs, ks_, vs_ = qkv[:, :w["Hq"]], qkv[:, w["Hq"]:w["Hq"] + w["Hkv"]], qkv[:, w["Hq"] + w["Hkv"]:]
+    fs = lambda: plan(qs, ks_, vs_, m["cu_q"], m["cu_kv"], out=wide[:, :w["Hq"]], lse=lse, B=w["B"])
+    _, per_s = time_replays([fs], reps, 2)
+
     def roundtrip():  # the D2H + host cumsum + H2D path the grid-sizing issue describes
         lens_h = (m["cu_q"][1:w["B"] + 1] - m["cu_q"][:w["B"]]).cpu().numpy()
         tl = [(b << 16) | t for b, L in enumerate(lens_h) for t in range(-(-int(L) // tq))]
@@ -344,6 +356,7 @@ def prefill_measure(args, reps=10):
                 live_tiles=len(tiles) * w["Hkv"],
                 scheduled_persistent_us=round(med(per_p) * 1e3, 1),
                 exact_grid_us=round(med(per_e) * 1e3, 1),
+                fused_qkv_strided_us=round(med(per_s) * 1e3, 1),
                 exact_grid_with_host_roundtrip_us=round(med(per_r) * 1e3, 1))
 
 
@@ -454,8 +467,17 @@ def mask_measure():
     out = torch.empty((33, 1, 1, 16384), dtype=torch.bool, device="cuda")
     f = lambda: V.padding_mask(cu, 33, 16384, out=out)
     _, per = time_replays([f], 50, 5)
+    # cross attention: query-side and key-side masks in one launch (key
+    # lengths: the same values in reverse order)
+    cu_k = torch.from_numpy(I.cu_from_lengths(lens[::-1].copy(), 65,
+                                              [-1, 2**31 - 1, int(lens.sum())])).cuda()
+    out_k = torch.empty_like(out)
+    fc = lambda: V.cross_padding_masks(cu, cu_k, 33, 16384, 16384, out_q=out, out_kv=out_k)
+    _, per_c = time_replays([fc], 50, 5)
     return dict(workload="padding mask B=33, max_seqlen=16384 (540672 bytes)",
-                us=round(sorted(per)[len(per) // 2] * 1e3, 2))
+                us=round(sorted(per)[len(per) // 2] * 1e3, 2),
+                cross_us=round(sorted(per_c)[len(per_c) // 2] * 1e3, 2),
+                cross_workload="query-side and key-side masks, B=33, 16384 each (1081344 bytes)")
 
 
 def gathered_measure(steps=50, **plan_opts):
