@@ -102,7 +102,7 @@ typedef struct {
                                schedule of live tiles on a persistent grid */
   int backward;             /* 1: also size the plan for vattn_backward (allocates the
                                row-wise <dO, O> buffer, B_max * s_max_q * Hq floats);
-                               D in {32, 64, 128} and G <= 256 only */
+                               G <= 256, and G <= 128 at D = 256 */
 } vattn_plan_opts;
 
 typedef struct {
@@ -125,9 +125,11 @@ typedef struct {
   int threads;         /* threads per workgroup of the main kernel */
   int prefill_persistent; /* prefill: 1 = schedule kernel + persistent grid of `grid` */
   int backward;        /* 1 if the plan serves vattn_backward */
-  int bwd_q_tokens_per_tile; /* backward dq kernel: query tokens per workgroup (256 / G) */
+  int bwd_q_tokens_per_tile; /* backward dq kernel: query tokens per workgroup
+                                (256 / G; 128 / G at D = 256) */
   int bwd_grid_dq;     /* backward: workgroups of the dq kernel */
-  int bwd_grid_dkdv;   /* backward: workgroups of the dk/dv kernel (128 keys each) */
+  int bwd_grid_dkdv;   /* backward: workgroups of the dk/dv kernel (128 keys each; at
+                          D = 256 two per key tile, one per 128-column slice) */
   long long scratch_bytes; /* device bytes owned by the plan */
 } vattn_plan_info;
 

@@ -101,7 +101,8 @@ def test_pure_cpp_plan_test(tmp_path):
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D", [(1, 100, 8, 8, 64), (16, 4096, 32, 8, 128),
-                                          (3, 1000, 12, 4, 32), (64, 1, 128, 1, 128)])
+                                          (3, 1000, 12, 4, 32), (64, 1, 128, 1, 128),
+                                          (5, 700, 16, 2, 256)])
 def test_describe_backward_grids(B, S, Hq, Hkv, D):
     """Backward plans: the dq grid follows the forward's grid rule at 256 rows
     per workgroup, the dk/dv grid covers 128-key tiles, and the plan's scratch
@@ -111,17 +112,19 @@ def test_describe_backward_grids(B, S, Hq, Hkv, D):
     base = V.describe_plan(B, S, S, Hq, Hkv, D, 1, n_cu_override=256)
     d = V.describe_plan(B, S, S, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
     G = Hq // Hkv
-    g = choose_prefill_grid(B, S, Hkv, 256 // G)
-    assert d["backward"] == 1 and d["bwd_q_tokens_per_tile"] == 256 // G
-    assert d["bwd_grid_dq"] == 8 * -(-(B * Hkv) // 8) * g["n_qtiles"]
-    assert d["bwd_grid_dkdv"] == 8 * -(-(B * Hkv) // 8) * -(-S // 128)
+    rows, slices = (256, 1) if D <= 128 else (128, 2)   # 128-column slices at D = 256
+    g = choose_prefill_grid(B, S, Hkv, rows // G)
+    assert d["backward"] == 1 and d["bwd_q_tokens_per_tile"] == rows // G
+    assert d["bwd_grid_dq"] == 8 * -(-(B * Hkv) // 8) * g["n_qtiles"] * slices
+    assert d["bwd_grid_dkdv"] == 8 * -(-(B * Hkv) // 8) * -(-S // 128) * slices
     assert d["scratch_bytes"] == base["scratch_bytes"] + 256 + 4 * B * S * Hq
     assert base["backward"] == 0 and base["bwd_grid_dq"] == 0
 
 
-@pytest.mark.parametrize("s_max_q,Hq,Hkv,D", [(64, 8, 2, 256), (1, 512, 1, 64)])
+@pytest.mark.parametrize("s_max_q,Hq,Hkv,D", [(1, 256, 1, 256), (1, 512, 1, 64)])
 def test_backward_plan_limits(s_max_q, Hq, Hkv, D):
-    """D = 256 and G > 256 have no backward; the forward plan is fine."""
+    """G above the dq workgroup's rows (128 at D = 256, else 256) has no
+    backward; the (decode) forward plan is fine."""
     import varlen_gqa_attention_amd as V
     _lib()
     with pytest.raises(V.VattnError) as e:

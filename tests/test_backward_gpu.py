@@ -68,7 +68,7 @@ K_LENS = [70, 1, 5, 129, 250, 20, 0, 65]
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("G", [1, 4, 8])
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_backward_matches_oracle(D, G, causal):
     import varlen_gqa_attention_amd as V
     Hkv = 2
@@ -81,7 +81,7 @@ def test_backward_matches_oracle(D, G, causal):
     _check(B, cu_q, cu_k, q, k, v, dout, dq, dk, dv, causal, f"D={D} G={G}")
 
 
-@pytest.mark.parametrize("G,D", [(8, 128), (2, 64), (16, 128)])
+@pytest.mark.parametrize("G,D", [(8, 128), (2, 64), (16, 128), (4, 256)])
 def test_backward_several_tiles_per_sequence(G, D):
     """Sequences spanning several query tiles, key tiles and 64-row steps."""
     import varlen_gqa_attention_amd as V

@@ -108,21 +108,34 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
 // ---------------------------------------------------------------------------
 // dq kernel (also writes delta)
 // ---------------------------------------------------------------------------
+// Waves of the dq kernel: 8 (two per SIMD) up to D = 128; at D = 256 a wave
+// needs a SIMD's whole register file.
 template <int D>
-__global__ __launch_bounds__((BwdCfg<D, 8>::THREADS)) void bwd_dq_kernel(BwdArgs a) {
-  using C = BwdCfg<D, 8>;  // 8 waves of 32 rows, two per SIMD
-  constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
+constexpr int dq_waves() { return D <= 128 ? 8 : 4; }
+
+template <int D>
+__global__ __launch_bounds__((BwdCfg<D, dq_waves<D>()>::THREADS)) void bwd_dq_kernel(BwdArgs a) {
+  using C = BwdCfg<D, dq_waves<D>()>;  // waves of 32 rows
+  constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, CH = C::CH;
   constexpr int PF = KS < 2 ? KS : 2;  // k-steps of LDS reads in flight
+  // At D = 256 a workgroup accumulates one 128-column slice of dQ (two
+  // workgroups per query tile, each recomputing S and dP over the full D),
+  // so that Q, dO and the dQ accumulators fit one wave's registers.
+  constexpr int DS = D <= 128 ? D : 128;  // dQ columns per workgroup
+  constexpr int NSL = D / DS;
+  constexpr int DBLK = DS / 32;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * C::TILE_BYTES];
 
   const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
-  const int u = x + 8 * (p / a.n_qtiles);
+  const int per_unit = a.n_qtiles * NSL;
+  const int u = x + 8 * (p / per_unit);
   if (u >= a.B_max * a.Hkv) return;
-  const int b = u / a.Hkv, hk = u % a.Hkv, qt = a.n_qtiles - 1 - p % a.n_qtiles;
+  const int b = u / a.Hkv, hk = u % a.Hkv;
+  const int qt = a.n_qtiles - 1 - (p % per_unit) / NSL, sl = (p % per_unit) % NSL;
   if (b >= a.B) return;
   const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
   const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
-  if (qt == 0 && hk == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
+  if (qt == 0 && hk == 0 && sl == 0 && threadIdx.x == 0) report(a.err, sq.flags | sk.flags);
   const int Lq = sq.len, Lk = sk.len;
   const int t0 = qt * a.tq;
   if (t0 >= Lq) return;
@@ -194,7 +207,8 @@ __global__ __launch_bounds__((BwdCfg<D, 8>::THREADS)) void bwd_dq_kernel(BwdArgs
   bwd_wait_vmem();
 
   delta = sum_xor32(delta);
-  if (row_ok && lane < 32) a.delta[((int64_t)b * a.s_max_q + tok) * a.Hq + hq] = delta;
+  if (row_ok && lane < 32 && sl == 0)
+    a.delta[((int64_t)b * a.s_max_q + tok) * a.Hq + hq] = delta;
   // exponent offset in base 2; a row without visible keys (lse = -inf) gets
   // +inf so that every weight is exp2(-inf) = 0
   const float lse2 = (lse == kNegInf) ? __builtin_inff() : lse * kLog2e;
@@ -248,7 +262,8 @@ __global__ __launch_bounds__((BwdCfg<D, 8>::THREADS)) void bwd_dq_kernel(BwdArgs
       bf16x8 kt[2][DBLK];
       auto rdt = [&](int h) {
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) kt[h][db] = frag_tr<D>(lk, 2 * kb + h, db, lane);
+        for (int db = 0; db < DBLK; ++db)
+          kt[h][db] = frag_tr<D>(lk, 2 * kb + h, sl * DBLK + db, lane);
       };
       rdt(0);
       // P and dS (lane: one row; keys key0 + 32 kb + 8 (i/4) + 4 (lane/32) + i%4)
@@ -277,7 +292,7 @@ __global__ __launch_bounds__((BwdCfg<D, 8>::THREADS)) void bwd_dq_kernel(BwdArgs
 
   // epilogue: lane holds dQ^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][row]
   if (!row_ok) return;
-  uint16_t* op = a.dq + qrow * a.dq_rs + hq * D + 4 * (lane >> 5);
+  uint16_t* op = a.dq + qrow * a.dq_rs + hq * D + sl * DS + 4 * (lane >> 5);
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -295,16 +310,30 @@ __global__ __launch_bounds__((BwdCfg<D, 8>::THREADS)) void bwd_dq_kernel(BwdArgs
 template <int D>
 __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BwdCfg<D>;
-  constexpr int BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK, CH = C::CH;
+  constexpr int CPR = C::CPR, KS = C::KS;
   constexpr int KEYS = 32 * C::NW;                  // keys per workgroup
   constexpr int PF = KS < 2 ? KS : 2;                // k-steps of LDS reads in flight
-  constexpr int STAGE = 2 * C::TILE_BYTES + 2 * BN * 4;  // Q, dO tiles + lse2, delta rows
+  // Up to D = 128 a step covers 64 query rows as two pipelined 32-row
+  // halves and a workgroup accumulates all of D. At D = 256 the registers of
+  // K, V, dK and dV do not fit beside that: a workgroup accumulates one
+  // 128-wide slice of dK, dV (two workgroups per key tile, each recomputing
+  // S and dP over the full D) and a step covers 32 rows.
+  constexpr int RBS = D <= 128 ? 2 : 1;              // 32-row blocks per step
+  constexpr int BN = 32 * RBS;                        // query rows per step
+  constexpr int DS = D <= 128 ? D : 128;              // dK / dV columns per workgroup
+  constexpr int NSL = D / DS;                         // column slices
+  constexpr int DBLK = DS / 32;                       // 32-wide blocks of the slice
+  constexpr int TILE = BN * D * 2;                    // one staged Q (or dO) tile
+  constexpr int CH = (BN * CPR + C::THREADS - 1) / C::THREADS;
+  constexpr int STAGE = 2 * TILE + 2 * BN * 4;       // Q, dO tiles + lse2, delta rows
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
 
   const int x = blockIdx.x & 7, p = blockIdx.x >> 3;
-  const int u = x + 8 * (p / a.n_ktiles);
+  const int per_unit = a.n_ktiles * NSL;
+  const int u = x + 8 * (p / per_unit);
   if (u >= a.B_max * a.Hkv) return;
-  const int b = u / a.Hkv, hk = u % a.Hkv, kt = p % a.n_ktiles;
+  const int b = u / a.Hkv, hk = u % a.Hkv;
+  const int kt = (p % per_unit) / NSL, sl = (p % per_unit) % NSL;
   if (b >= a.B) return;
   const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
   const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
@@ -368,11 +397,10 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
       if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
       const int r = q / CPR, c = q % CPR;
       *reinterpret_cast<u32x4*>(s0 + r * D * 2 + swz_rows<D>(r, c) * 16) = stq[i];
-      *reinterpret_cast<u32x4*>(s0 + C::TILE_BYTES + r * D * 2 + swz_rows<D>(r, c) * 16) =
-          std_[i];
+      *reinterpret_cast<u32x4*>(s0 + TILE + r * D * 2 + swz_rows<D>(r, c) * 16) = std_[i];
     }
     if (threadIdx.x < BN) {
-      float* rows = reinterpret_cast<float*>(s0 + 2 * C::TILE_BYTES);
+      float* rows = reinterpret_cast<float*>(s0 + 2 * TILE);
       rows[threadIdx.x] = st_lse;
       rows[BN + threadIdx.x] = st_dl;
     }
@@ -396,8 +424,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
       if (it + 2 < n_it) load_step(it + 2);
     }
     const uint8_t* lq = lds + (it & 1) * STAGE;
-    const uint8_t* ldo = lq + C::TILE_BYTES;
-    const float* lrow = reinterpret_cast<const float*>(lq + 2 * C::TILE_BYTES);
+    const uint8_t* ldo = lq + TILE;
+    const float* lrow = reinterpret_cast<const float*>(lq + 2 * TILE);
     const int tbase = t_first + (it / a.G) * BN;
     // Per step, two 32-row halves in a software pipeline, so that each
     // half's softmax-gradient VALU work runs under the other half's MFMAs:
@@ -425,8 +453,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
     auto rdt = [&](int step) {
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        dt[step][db] = frag_tr<D>(ldo, step, db, lane);
-        qt[step][db] = frag_tr<D>(lq, step, db, lane);
+        dt[step][db] = frag_tr<D>(ldo, step, sl * DBLK + db, lane);
+        qt[step][db] = frag_tr<D>(lq, step, sl * DBLK + db, lane);
       }
     };
     auto mmt = [&](int step) {
@@ -463,58 +491,80 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
         s[rb][i] = pv * (dp[rb][i] - d4[g][e]);
       }
     };
-    // A
+    if constexpr (RBS == 2) {
+      // A
 #pragma unroll
-    for (int ks = 0; ks < PF; ++ks) rd(0, ks);
+      for (int ks = 0; ks < PF; ++ks) rd(0, ks);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) rd(0, ks + PF);
-      else rd(1, ks + PF - KS);
-      __builtin_amdgcn_sched_barrier(0);
-      mm(0, ks);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // B: two entries of rows 0-31 per k-step of rows 32-63 (the order of
-    // the source is kept by the scheduling barriers)
-    rows_of(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) rd(1, ks + PF);
-      if (ks == KS - 2) rdt(0);
-      if (ks == KS - 1) rdt(1);
-      mm(1, ks);
-#pragma unroll
-      for (int i0 = 16 * ks / KS; i0 < 16 * (ks + 1) / KS; i0 += 2) grad(0, i0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // C: two entries of rows 32-63 per d block of the rows 0-31 products
-    rows_of(1);
-#pragma unroll
-    for (int step = 0; step < 2; ++step) {
-      const bf16x8 bp = pack_acc(pp[0], step);
-      const bf16x8 bds = pack_acc(s[0], step);
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        if (step == 1 && db == 0) rdt(2);
-        if (step == 1 && db == DBLK - 1) rdt(3);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[step][db], bp, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[step][db], bds, dk[db], 0, 0, 0);
-        const int j = step * DBLK + db;
-#pragma unroll
-        for (int i0 = 16 * j / (2 * DBLK); i0 < 16 * (j + 1) / (2 * DBLK); i0 += 2) grad(1, i0);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) rd(0, ks + PF);
+        else rd(1, ks + PF - KS);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(0, ks);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // B: two entries of rows 0-31 per k-step of rows 32-63 (the order of
+      // the source is kept by the scheduling barriers)
+      rows_of(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) rd(1, ks + PF);
+        if (ks == KS - 2) rdt(0);
+        if (ks == KS - 1) rdt(1);
+        mm(1, ks);
+#pragma unroll
+        for (int i0 = 16 * ks / KS; i0 < 16 * (ks + 1) / KS; i0 += 2) grad(0, i0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // C: two entries of rows 32-63 per d block of the rows 0-31 products
+      rows_of(1);
+#pragma unroll
+      for (int step = 0; step < 2; ++step) {
+        const bf16x8 bp = pack_acc(pp[0], step);
+        const bf16x8 bds = pack_acc(s[0], step);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          if (step == 1 && db == 0) rdt(2);
+          if (step == 1 && db == DBLK - 1) rdt(3);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt[step][db], bp, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[step][db], bds, dk[db], 0, 0, 0);
+          const int j = step * DBLK + db;
+#pragma unroll
+          for (int i0 = 16 * j / (2 * DBLK); i0 < 16 * (j + 1) / (2 * DBLK); i0 += 2) grad(1, i0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // D
+      mmt(2);
+      mmt(3);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // one 32-row block per step: S, dP, then P, dS, then dV, dK
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) rd(0, ks);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + PF < KS) rd(0, ks + PF);
+        __builtin_amdgcn_sched_barrier(0);
+        mm(0, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      rdt(0);
+      rows_of(0);
+#pragma unroll
+      for (int i0 = 0; i0 < 16; i0 += 2) grad(0, i0);
+      rdt(1);
+      __builtin_amdgcn_sched_barrier(0);
+      mmt(0);
+      mmt(1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // D
-    mmt(2);
-    mmt(3);
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // epilogue: lane holds dK^T / dV^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][key]
   if (!key_ok) return;
-  uint16_t* kp = a.dk + krow * a.dk_rs + hk * D + 4 * (lane >> 5);
-  uint16_t* vp = a.dv + krow * a.dv_rs + hk * D + 4 * (lane >> 5);
+  uint16_t* kp = a.dk + krow * a.dk_rs + hk * D + sl * DS + 4 * (lane >> 5);
+  uint16_t* vp = a.dv + krow * a.dv_rs + hk * D + sl * DS + 4 * (lane >> 5);
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -535,7 +585,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, int grid_dq, int grid_dkdv, hip
   using C = BwdCfg<D>;
   // with measurement events, ev0 is stamped at the dq kernel's start and ev1
   // at the dk/dv kernel's end (the whole backward)
-  constexpr int DQ_THREADS = BwdCfg<D, 8>::THREADS;
+  constexpr int DQ_THREADS = BwdCfg<D, dq_waves<D>()>::THREADS;
   if (ev0)
     hipExtLaunchKernelGGL(bwd_dq_kernel<D>, dim3(grid_dq), dim3(DQ_THREADS), 0, st, ev0, nullptr,
                           0, a);
@@ -557,6 +607,7 @@ hipError_t launch_backward(const BwdArgs& a, int D, int grid_dq, int grid_dkdv, 
     case 32: return launch_bwd_d<32>(a, grid_dq, grid_dkdv, st, ev0, ev1);
     case 64: return launch_bwd_d<64>(a, grid_dq, grid_dkdv, st, ev0, ev1);
     case 128: return launch_bwd_d<128>(a, grid_dq, grid_dkdv, st, ev0, ev1);
+    case 256: return launch_bwd_d<256>(a, grid_dq, grid_dkdv, st, ev0, ev1);
   }
   return hipErrorInvalidValue;
 }

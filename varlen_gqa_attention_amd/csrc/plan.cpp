@@ -136,14 +136,15 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     }
   }
   if (o.backward == 1) {
-    // backward kernels: dq workgroups of 256 rows (G heads folded), dk/dv
-    // workgroups of 128 keys; the grids cover B_max x s_max like the forward
-    if (D > 128 || G > kBwdRows) return VATTN_ERR_UNSUPPORTED;
+    // backward kernels: dq workgroups of bwd_rows(D) rows (G heads folded),
+    // dk/dv workgroups of 128 keys, each of both over one 128-column slice of
+    // its output at D = 256; the grids cover B_max x s_max like the forward
+    if (G > bwd_rows(D)) return VATTN_ERR_UNSUPPORTED;
     in.backward = 1;
-    in.bwd_q_tokens_per_tile = kBwdRows / G;
+    in.bwd_q_tokens_per_tile = bwd_rows(D) / G;
     const int64_t units8 = 8 * (((int64_t)B_max * Hkv + 7) / 8);
-    const int64_t g_dq = units8 * cdiv(s_max_q, in.bwd_q_tokens_per_tile);
-    const int64_t g_kv = units8 * cdiv(s_max_kv, kBwdKeys);
+    const int64_t g_dq = units8 * cdiv(s_max_q, in.bwd_q_tokens_per_tile) * bwd_slices(D);
+    const int64_t g_kv = units8 * cdiv(s_max_kv, kBwdKeys) * bwd_slices(D);
     if (g_dq > (1LL << 31) - 1 || g_kv > (1LL << 31) - 1) return VATTN_ERR_UNSUPPORTED;
     in.bwd_grid_dq = (int)g_dq;
     in.bwd_grid_dkdv = (int)g_kv;

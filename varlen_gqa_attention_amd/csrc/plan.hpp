@@ -17,10 +17,12 @@ constexpr int kMinChunkTiles = 16;     // split rule: fewest KV tiles per split
 // of 32 rows; threads per prefill workgroup
 constexpr int prefill_rows(int D) { return D <= 128 ? 256 : 128; }
 constexpr int prefill_threads(int D) { return D <= 128 ? 512 : 256; }
-// backward: query rows (heads x tokens) per dq workgroup (8 waves of 32) and
-// keys per dk/dv workgroup (4 waves of 32)
-constexpr int kBwdRows = 256;
+// backward: query rows (heads x tokens) per dq workgroup (8 waves of 32, 4
+// at D = 256), keys per dk/dv workgroup (4 waves of 32) and dk/dv workgroups
+// per key tile (two 128-column slices at D = 256)
+constexpr int bwd_rows(int D) { return D <= 128 ? 256 : 128; }
 constexpr int kBwdKeys = 128;
+constexpr int bwd_slices(int D) { return D <= 128 ? 1 : D / 128; }
 // largest query-tile count per sequence the on-device prefill schedule handles
 constexpr int kSchedMaxQtiles = 8192;
 
