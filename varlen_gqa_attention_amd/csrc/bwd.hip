@@ -20,11 +20,15 @@
 //    the transposed LDS read. Its prologue also computes delta_i from dO and
 //    O and stores it for the second kernel.
 //  * dk/dv kernel: workgroup = (sequence, KV head, 128-key tile), 32 keys per
-//    wave with K and V of those keys in registers. It walks the query rows
-//    that can see its keys (64 tokens of one query head per step, all G
-//    heads): S = Q K^T and dP = dO V^T with Q and dO rows from LDS, P and dS
-//    (one key per lane), then dV^T += dO^T P and dK^T += Q^T dS with dO^T and
-//    Q^T from the transposed LDS read.
+//    wave (one wave per SIMD) with K and V of those keys in registers. It
+//    walks the query rows that can see its keys (64 tokens of one query head
+//    per step, all G heads): S = Q K^T and dP = dO V^T with Q and dO rows
+//    from LDS, P and dS (one key per lane), then dV^T += dO^T P and
+//    dK^T += Q^T dS with dO^T and Q^T from the transposed LDS read; the two
+//    32-row halves of a step are software-pipelined.
+//  * At D = 256 each workgroup of either kernel produces one 128-column slice
+//    of its output (recomputing S and dP over the full D), the dq kernel runs
+//    4 waves and the dk/dv kernel steps over 32 rows, to fit the registers.
 // Every contraction is v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
 // dS are rounded to bf16 as MFMA operands. Tiles reach a two-stage LDS ring
 // through registers (loads two steps ahead, one barrier per step).
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   }
 
   // query rows that can see a key of this tile: tokens from t_first (causal:
-  // key j0 needs token >= j0 - shift), 64 tokens of one query head per step
+  // key j0 needs token >= j0 - shift), BN tokens of one query head per step
   const int t_first = a.causal ? max(0, j0 - shift) : 0;
   const int n_tb = Lq > t_first ? (Lq - t_first + BN - 1) / BN : 0;
   const int n_it = n_tb * a.G;
