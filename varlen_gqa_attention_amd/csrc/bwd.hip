@@ -62,17 +62,17 @@ struct BwdCfg {
 };
 
 // A-operand fragment of a 32-row block of a row-major LDS tile (rows of D
-// bf16, swz_rows layout): lane holds row 32 blk + lane % 32, elements
+// bf16, swz_dual layout): lane holds row 32 blk + lane % 32, elements
 // 16 ks + 8 (lane / 32) .. + 8.
 template <int D>
 __device__ __forceinline__ bf16x8 frag_rows(const uint8_t* t, int blk, int ks, int lane) {
   const int r = 32 * blk + (lane & 31);
   const int c = 2 * ks + (lane >> 5);
   return __builtin_bit_cast(bf16x8,
-                            *reinterpret_cast<const u32x4*>(t + r * D * 2 + swz_rows<D>(r, c) * 16));
+                            *reinterpret_cast<const u32x4*>(t + r * D * 2 + swz_dual<D>(r, c) * 16));
 }
 
-// A-operand fragment of the transpose of a 64-row LDS tile (swz_rows layout)
+// A-operand fragment of the transpose of a 64-row LDS tile (swz_dual layout)
 // for k-step `step` (16 rows) and d block db: lane holds column
 // d = 32 db + lane % 32 at the 8 rows that the bf16 packing of a 32x32 MFMA
 // accumulator (see pack_acc) puts in lane / 32's half of that k-step.
@@ -84,8 +84,8 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint8_t* t, int step, int db, in
   const int r2 = r1 + 8;
   const int col = 32 * db + 16 * (g & 1) + 4 * (m16 & 3);
   const int ch = col >> 3, half = (col >> 2) & 1;
-  const bf16x4 x1 = bwd_read_tr(t + r1 * D * 2 + swz_rows<D>(r1, ch) * 16 + half * 8);
-  const bf16x4 x2 = bwd_read_tr(t + r2 * D * 2 + swz_rows<D>(r2, ch) * 16 + half * 8);
+  const bf16x4 x1 = bwd_read_tr(t + r1 * D * 2 + swz_dual<D>(r1, ch) * 16 + half * 8);
+  const bf16x4 x2 = bwd_read_tr(t + r2 * D * 2 + swz_dual<D>(r2, ch) * 16 + half * 8);
   return __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -203,8 +203,8 @@ __global__ __launch_bounds__((BwdCfg<D, dq_waves<D>()>::THREADS)) void bwd_dq_ke
       const int q = threadIdx.x + i * C::THREADS;
       if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
       const int r = q / CPR, c = q % CPR;
-      *reinterpret_cast<u32x4*>(sk_ + r * D * 2 + swz_rows<D>(r, c) * 16) = stk[i];
-      *reinterpret_cast<u32x4*>(sv_ + r * D * 2 + swz_rows<D>(r, c) * 16) = stv[i];
+      *reinterpret_cast<u32x4*>(sk_ + r * D * 2 + swz_dual<D>(r, c) * 16) = stk[i];
+      *reinterpret_cast<u32x4*>(sv_ + r * D * 2 + swz_dual<D>(r, c) * 16) = stv[i];
     }
   };
   if (ntiles > 0) load_tile(0);
@@ -400,8 +400,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
       const int q = threadIdx.x + i * C::THREADS;
       if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
       const int r = q / CPR, c = q % CPR;
-      *reinterpret_cast<u32x4*>(s0 + r * D * 2 + swz_rows<D>(r, c) * 16) = stq[i];
-      *reinterpret_cast<u32x4*>(s0 + TILE + r * D * 2 + swz_rows<D>(r, c) * 16) = std_[i];
+      *reinterpret_cast<u32x4*>(s0 + r * D * 2 + swz_dual<D>(r, c) * 16) = stq[i];
+      *reinterpret_cast<u32x4*>(s0 + TILE + r * D * 2 + swz_dual<D>(r, c) * 16) = std_[i];
     }
     if (threadIdx.x < BN) {
       float* rows = reinterpret_cast<float*>(s0 + 2 * TILE);

@@ -219,4 +219,18 @@ __device__ __forceinline__ int swz_tr32(int row, int chunk) {
   else return chunk;
 }
 
+// Pattern for tiles read both ways: row reads as the 32x32x16 MFMA operand
+// (16 lanes on 16 consecutive rows, one 16-byte chunk) and the transposed
+// read of the same tile (a half-wave on 4 consecutive rows x 4 consecutive
+// chunks). The XOR operand puts the low two row bits above the next two, so
+// any 16 consecutive rows and any 4 consecutive rows x 4 chunks land on
+// distinct 16-byte bank groups (checked by enumeration of both patterns).
+template <int D>
+__device__ __forceinline__ int swz_dual(int row, int chunk) {
+  constexpr int CPR = D / 8;
+  if constexpr (CPR >= 16) return chunk ^ (4 * (row & 3) + ((row >> 2) & 3));
+  else if constexpr (CPR == 8) return chunk ^ ((2 * (row & 3) + ((row >> 1) & 7)) & 7);
+  else return chunk ^ ((row >> 2) & 3);
+}
+
 }  // namespace vattn
