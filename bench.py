@@ -270,6 +270,41 @@ def cpu_baseline_long_decode(state, budget_s):
                        f"({dt:.2f} s each; K/V of bf16 values copied to host, untimed)")
 
 
+def cpu_baseline_prefill(budget_s):
+    """The oracle's forward and backward on one (sequence, query head) of the
+    causal varlen prefill workload (its longest sequence), as GFLOP/s of the
+    same algorithmic flop counts the GPU lines use (4 D and 8 D per visible
+    pair): the bounded sample of the prefill and backward rows."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import backward as BW
+    from varlen_gqa_attention_amd import inputs as I
+    w = I.varlen_prefill(0)
+    L = int(np.max(w["q_lens"]))
+    D = w["D"]
+    rng = np.random.default_rng(0)   # values of the sample (the timing does not depend on them)
+    q, k, v, do = (rng.standard_normal((L, D)) for _ in range(4))
+    vis = A.visible_keys(L, L, True)
+    pairs = int(vis.sum())
+    scale = 1.0 / np.sqrt(D)
+    out = {}
+    for name, fn, flop in (("prefill", lambda: A.attend_rows(q, k, v, vis, scale), 4 * D * pairs),
+                           ("backward", lambda: BW.backward_rows(q, k, v, do, vis, scale),
+                            8 * D * pairs)):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+        out[name] = dict(value=round(flop / dt / 1e9, 2), unit="GFLOP/s",
+                         sample=f"{n} call(s) on one query head of a {L}-token causal sequence "
+                                f"({dt:.2f} s each)")
+    return out
+
+
 def visible_pairs(q_lens, kv_lens):
     """(query, key) pairs a causal (bottom-right aligned) pass must compute:
     query i of a sequence sees keys j <= i + Lk - Lq, clamped to [0, Lk)."""
@@ -588,6 +623,8 @@ def main():
         line["padding_mask"] = mask_measure()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)
+        if not args.no_secondary:
+            line["cpu_baseline"]["secondary"] = cpu_baseline_prefill(min(5.0, args.cpu_budget))
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line))
