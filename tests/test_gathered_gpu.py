@@ -117,3 +117,32 @@ def test_gathered_needs_a_decode_plan():
     with pytest.raises(V.VattnError) as e:
         plan.gathered(q, k, k, cu, cu, torch.zeros(2, dtype=torch.int32, device="cuda"))
     assert e.value.status == -2
+
+
+def test_gathered_full_size_bench_configuration():
+    """The benchmark's gathered workload at full size (16 sequences, each
+    attending 2048 sorted rows of its own 32768-token history, Hq=32, Hkv=8,
+    D=128, default plan): every output against the oracle, which receives
+    the selected rows (gathered with torch indexing) and an identity list."""
+    import varlen_gqa_attention_amd as V
+    B, Hq, Hkv, D, hist, sel = 16, 32, 8, 128, 32768, 2048
+    plan = V.Plan(B, 1, sel, Hq, Hkv, D, False)
+    q = I.normal_bf16((B, Hq, D), 40, "cuda")
+    k = I.normal_bf16((B * hist, Hkv, D), 41, "cuda")
+    v = I.normal_bf16((B * hist, Hkv, D), 42, "cuda")
+    rng = I.rng(7, 0)
+    idx = np.concatenate([b * hist + np.sort(rng.choice(hist, sel, replace=False))
+                          for b in range(B)]).astype(np.int32)
+    cu_q = I.cu_from_lengths(np.ones(B, np.int64))
+    cu_idx = I.cu_from_lengths(np.full(B, sel))
+    print(f"[gathered full size] plan {plan.info['nsplit']} splits", flush=True)
+    out, lse = _run(plan, q, k, v, cu_q, cu_idx, idx, B)
+    assert plan.read_error() == 0
+    rows = torch.from_numpy(idx).cuda().long()
+    ks, vs = k[rows], v[rows]
+    ro, rl, wr, clamped = A.attend_gathered(
+        I.bf16_to_f64(q), I.bf16_to_f64(ks), I.bf16_to_f64(vs), cu_q, cu_idx,
+        np.arange(B * sel, dtype=np.int64), B, s_max_kv=sel)
+    assert not clamped and wr.all()
+    assert_out_close(I.bf16_to_f64(out), ro)
+    assert_lse_close(lse.cpu().numpy(), rl)

@@ -104,3 +104,29 @@ def test_invalid_strides_are_rejected():
     assert call(0, 0, 0, Hq * D - 64) == -1
     assert call(0, 0, 0, 0) == 0                      # 0 = packed
     torch.cuda.synchronize()
+
+
+def test_prefill_full_size_on_fused_qkv_equals_packed_bitwise():
+    """The benchmark's causal varlen prefill at full size with q, k, v as
+    slices of one fused QKV buffer and out inside a wider buffer: bit-equal
+    to the packed call."""
+    import varlen_gqa_attention_amd as V
+    w = I.varlen_prefill(0)
+    m = I.materialise(w, 0, "cuda")
+    Hq, Hkv, D = w["Hq"], w["Hkv"], w["D"]
+    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], Hq, Hkv, D, True)
+    out_p, lse_p = plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], B=w["B"])
+    T = m["q"].shape[0]
+    qkv = torch.empty(T, Hq + 2 * Hkv, D, dtype=torch.bfloat16, device="cuda")
+    qkv[:, :Hq] = m["q"]
+    qkv[:, Hq:Hq + Hkv] = m["k"]
+    qkv[:, Hq + Hkv:] = m["v"]
+    buf, out_s = _wide_out(T, Hq, D)
+    lse_s = torch.empty(T, Hq, device="cuda")
+    plan(qkv[:, :Hq], qkv[:, Hq:Hq + Hkv], qkv[:, Hq + Hkv:], m["cu_q"], m["cu_kv"], out=out_s,
+         lse=lse_s, B=w["B"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_p.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse_p, lse_s)
+    raw = buf.view(torch.int16)
+    assert bool((raw[:, 0] == SENT).all()) and bool((raw[:, Hq + 1:] == SENT).all())
