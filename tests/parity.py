@@ -7,14 +7,17 @@ oracle, widened to one bf16 ulp of the reference where that is larger (from
 exactly and NaN always fails.
 
 Gradients (bf16 dq, dk, dv) against the unrounded fp64 oracle: every element
-within 2e-2 + 2^-8 |ref|, and the whole tensor within 1e-2 relative in the
-Frobenius norm. Derivation: the kernels round the softmax weights and dS to
-bf16 as MFMA operands (2^-9 relative each, random), take <dO, O> from the
-forward's bf16 output, and round the results to bf16 (the 2^-8 |ref| term);
-an emulation of exactly these roundings in fp64 (causal, L up to 2000, D 32
-and 128, N(0,1) inputs) gives element errors beyond the output rounding of at
-most 0.0094 and Frobenius ratios of 0.0021-0.0025, so both bounds hold a
-margin of 2x and 4x.
+within 2e-2 * sqrt(n) + 2^-8 |ref|, where n is the number of query heads
+whose contributions the element sums (1 for dq, G for dk and dv), and the
+whole tensor within 1e-2 relative in the Frobenius norm. Derivation: the
+kernels round the softmax weights and dS to bf16 as MFMA operands (2^-9
+relative each, random), take <dO, O> from the forward's bf16 output, and
+round the results to bf16 (the 2^-8 |ref| term); an fp64 emulation of exactly
+these roundings (causal, L up to 2000, D 32 and 128, N(0,1) inputs) gives
+per-head element errors beyond the output rounding of at most 0.0094 and
+Frobenius ratios of 0.0021-0.0027; dk and dv add G independent per-head
+errors, which grow as sqrt(G) (emulated: 0.0068 at G = 1, 0.020 at G = 16),
+while the Frobenius ratio does not grow with G.
 """
 import numpy as np
 
@@ -61,13 +64,13 @@ def assert_lse_close(got, ref, what=""):
     return float(err.max()) if err.size else 0.0
 
 
-def assert_grad_close(got, ref, what=""):
+def assert_grad_close(got, ref, what="", heads=1):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert not np.isnan(got).any(), f"{what}: NaN in gradient"
     err = np.abs(got - ref)
-    bad = err > GRAD_ATOL + GRAD_RTOL * np.abs(ref)
+    bad = err > GRAD_ATOL * np.sqrt(heads) + GRAD_RTOL * np.abs(ref)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} gradients out of tolerance; max err "
