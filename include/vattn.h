@@ -246,9 +246,10 @@ vattn_status vattn_execute_strided(vattn_plan_t p, int B,
  * Rows of dq of every sequence are written (0 for a row without visible
  * keys); rows of dk, dv of every sequence are written (0 for keys no query
  * sees); rows outside all sequences are not touched. Sequences must not share
- * K/V rows. Strides as vattn_execute_strided (0 = packed; >= H * D and a
- * multiple of 8; q_rs applies to q, out_rs to out, dout_rs to dout, and so
- * on); q_rows bounds q, out, dout, lse and dq, kv_rows bounds k, v, dk and dv.
+ * K/V rows. Strides as vattn_execute_strided (0 = packed; >= H * D, a
+ * multiple of 8 and, here, below 2^24 elements; q_rs applies to q, out_rs to
+ * out, dout_rs to dout, and so on); q_rows bounds q, out, dout, lse and dq,
+ * kv_rows bounds k, v, dk and dv.
  * Needs a plan made with opts.backward = 1 (VATTN_ERR_UNSUPPORTED otherwise).
  * Enqueues two kernels (dq, which also stores <dout_i, out_i> in the plan's
  * scratch, then dk/dv) and returns: no allocation, no synchronisation, no

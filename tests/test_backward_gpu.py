@@ -154,6 +154,7 @@ def test_backward_needs_a_backward_plan_and_valid_strides():
                                 P(lse), P(cu), P(cu), P(q), 0, P(k), dk_rs, P(k), 0, 8, 8, None)
     assert call(Hq * D - 8, 0) == -1         # rows would overlap
     assert call(0, Hkv * D + 4) == -1        # not 16-byte aligned
+    assert call(1 << 24, 0) == -1            # beyond the 24-bit row offsets
     assert call(0, 0) == 0
     torch.cuda.synchronize()
 

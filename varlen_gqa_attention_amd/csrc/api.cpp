@@ -356,7 +356,8 @@ vattn_status vattn_backward(vattn_plan_t p, int B, const void* q, int64_t q_row_
   int64_t r[8];
   for (int i = 0; i < 8; ++i) {
     r[i] = rs[i] ? rs[i] : packed[i];
-    if (r[i] < packed[i] || (r[i] & 7)) return VATTN_ERR_INVALID_ARG;
+    // the dk/dv kernel forms in-step row offsets with 24-bit multiplies
+    if (r[i] < packed[i] || (r[i] & 7) || r[i] >= (int64_t(1) << 24)) return VATTN_ERR_INVALID_ARG;
   }
   if (B == 0) return VATTN_OK;
   if (!dout || !dq || !dk || !dv) return VATTN_ERR_INVALID_ARG;

@@ -45,6 +45,15 @@ __device__ __forceinline__ bf16x4 bwd_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base must be the same for the whole wave). Completion
+// is counted by vmcnt like any vector-memory load.
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
 __device__ __forceinline__ void bwd_wait_vmem() {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 }
@@ -370,47 +379,48 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   const int n_tb = Lq > t_first ? (Lq - t_first + BN - 1) / BN : 0;
   const int n_it = n_tb * a.G;
 
-  u32x4 stq[CH], std_[CH];
+  // Staging: the Q and dO tiles of a step go straight from global memory to
+  // LDS (lds_dma16); the lane that fills slot (row r, position c') of the
+  // swizzled tile loads chunk swz_dual(r, c') of the row (the swizzle is an
+  // XOR, its own inverse). Rows past the sequence are clamped to its last
+  // row; they get lse = +inf below, so they carry weight 0. lse and delta of
+  // the step's rows come through registers and are written (lse in base 2)
+  // one step later, so their latency is not waited on at issue.
   float st_lse = 0.f, st_dl = 0.f;
-  auto load_step = [&](int it) {
+  bool st_dead = false;
+  auto issue_step = [&](int it, uint8_t* dst) {
     const int tb = it / a.G, hq = hk * a.G + it % a.G;
     const int tbase = t_first + tb * BN;
+    const int rlim = Lq - 1 - tbase;
+    const int64_t t0 = (int64_t)sq.start + tbase;
+    const uint16_t* qb = a.q + t0 * a.q_rs + hq * D;
+    const uint16_t* db = a.dout + t0 * a.do_rs + hq * D;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
-      const int r = q / CPR, c = q % CPR;
-      const int64_t t = sq.start + min(tbase + r, Lq - 1);
-      stq[i] = ld16(a.q + t * a.q_rs + hq * D + 8 * c);
-      std_[i] = ld16(a.dout + t * a.do_rs + hq * D + 8 * c);
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;  // whole waves
+      const int r = q / CPR;
+      const uint32_t rr = (uint32_t)min(r, rlim);
+      const uint32_t c8 = 8 * swz_dual<D>(r, q % CPR);
+      uint8_t* base = dst + (q - lane) * 16;
+      lds_dma16(qb + (__umul24(rr, (uint32_t)a.q_rs) + c8), base);
+      lds_dma16(db + (__umul24(rr, (uint32_t)a.do_rs) + c8), base + TILE);
     }
     if (threadIdx.x < BN) {
-      const int tk = tbase + threadIdx.x;
-      const int tc = min(tk, Lq - 1);
-      const float ls = a.lse[((int64_t)sq.start + tc) * a.Hq + hq];
-      // rows past the sequence, or without visible keys, get weight 0
-      st_lse = (tk >= Lq || ls == kNegInf) ? __builtin_inff() : ls * kLog2e;
-      st_dl = a.delta[((int64_t)b * a.s_max_q + tc) * a.Hq + hq];
+      const uint32_t rr = (uint32_t)min((int)threadIdx.x, rlim);
+      st_dead = (int)threadIdx.x > rlim;
+      st_lse = a.lse[t0 * a.Hq + hq + __umul24(rr, (uint32_t)a.Hq)];
+      st_dl = a.delta[((int64_t)b * a.s_max_q + tbase) * a.Hq + hq + __umul24(rr, (uint32_t)a.Hq)];
     }
   };
-  auto store_step = [&](int it) {
-    uint8_t* s0 = lds + (it & 1) * STAGE;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
-      const int r = q / CPR, c = q % CPR;
-      *reinterpret_cast<u32x4*>(s0 + r * D * 2 + swz_dual<D>(r, c) * 16) = stq[i];
-      *reinterpret_cast<u32x4*>(s0 + TILE + r * D * 2 + swz_dual<D>(r, c) * 16) = std_[i];
-    }
+  auto put_rows = [&](uint8_t* dst) {
     if (threadIdx.x < BN) {
-      float* rows = reinterpret_cast<float*>(s0 + 2 * TILE);
-      rows[threadIdx.x] = st_lse;
+      float* rows = reinterpret_cast<float*>(dst + 2 * TILE);
+      // rows past the sequence, or without visible keys, get weight 0
+      rows[threadIdx.x] = (st_dead || st_lse == kNegInf) ? __builtin_inff() : st_lse * kLog2e;
       rows[BN + threadIdx.x] = st_dl;
     }
   };
-  if (n_it > 0) load_step(0);
-  bwd_wait_vmem();
 
   f32x16 dk[DBLK], dv[DBLK];
 #pragma unroll
@@ -418,16 +428,11 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
 #pragma unroll
     for (int j = 0; j < 16; ++j) dk[i][j] = dv[i][j] = 0.f;
 
-  if (n_it > 0) store_step(0);
-  if (n_it > 1) load_step(1);
-
-  for (int it = 0; it < n_it; ++it) {
-    __syncthreads();
-    if (it + 1 < n_it) {
-      store_step(it + 1);
-      if (it + 2 < n_it) load_step(it + 2);
-    }
-    const uint8_t* lq = lds + (it & 1) * STAGE;
+  // One step: issue the next step's loads into the other stage, then compute
+  // from this one. The two stages are disjoint (restrict), which lets the
+  // compiler read `lq` while the direct loads into `nxt` are in flight.
+  auto step = [&](int it, const uint8_t* __restrict__ lq, uint8_t* __restrict__ nxt) {
+    if (it + 1 < n_it) issue_step(it + 1, nxt);
     const uint8_t* ldo = lq + TILE;
     const float* lrow = reinterpret_cast<const float*>(lq + 2 * TILE);
     const int tbase = t_first + (it / a.G) * BN;
@@ -483,14 +488,15 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
         d4[g] = *reinterpret_cast<const f32x4*>(lrow + BN + r0);
       }
     };
+    // visible iff key <= min(Lk - 1, vlim + rr) with rr = row - 4 (lane / 32):
+    // one compare, and the exponent of a hidden entry is -inf (no branch)
+    const int vlim = a.causal ? tbase + shift + 4 * (lane >> 5) : Lk;
     auto grad = [&](int rb, int i0) {
 #pragma unroll
       for (int i = i0; i < i0 + 2; ++i) {
         const int g = i >> 2, e = i & 3;
-        const int row = 32 * rb + 8 * g + 4 * (lane >> 5) + e;
-        float pv = fast_exp2(fmaf(s[rb][i], a.c, -l4[g][e]));
-        const bool vis = key_ok && (!a.causal || key <= tbase + row + shift);
-        pv = vis ? pv : 0.f;
+        const bool vis = key <= min(Lk - 1, vlim + 32 * rb + 8 * g + e);
+        const float pv = fast_exp2(vis ? fmaf(s[rb][i], a.c, -l4[g][e]) : kNegInf);
         pp[rb][i] = pv;
         s[rb][i] = pv * (dp[rb][i] - d4[g][e]);
       }
@@ -499,6 +505,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
       // A
 #pragma unroll
       for (int ks = 0; ks < PF; ++ks) rd(0, ks);
+      rows_of(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + PF < KS) rd(0, ks + PF);
@@ -509,7 +516,6 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
       }
       // B: two entries of rows 0-31 per k-step of rows 32-63 (the order of
       // the source is kept by the scheduling barriers)
-      rows_of(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + PF < KS) rd(1, ks + PF);
@@ -563,6 +569,15 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
       mmt(1);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if (n_it > 0) issue_step(0, lds);
+  for (int it = 0; it < n_it; ++it) {
+    uint8_t* cur = lds + (it & 1) * STAGE;
+    bwd_wait_vmem();       // this wave's loads of step it have landed
+    put_rows(cur);
+    __syncthreads();       // every wave's have; stage (it + 1) & 1 is free
+    step(it, cur, lds + ((it + 1) & 1) * STAGE);
   }
 
   // epilogue: lane holds dK^T / dV^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][key]
