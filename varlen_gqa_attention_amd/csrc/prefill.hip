@@ -14,10 +14,10 @@
 // LDS as the A operand; Q^T held in registers), online softmax in base 2 with
 // per-lane row state (all of a lane's scores belong to one query row), then
 // O^T += V^T P^T where P^T is the S^T accumulator rounded to bf16 in place and
-// V^T comes from the gfx950 transposed LDS read. K/V tiles reach a two-stage
-// LDS ring through registers: the global loads of tile jt + 2 are in flight
-// while tile jt is computed, and land in LDS (swizzled, conflict-free) at the
-// start of the next iteration; one workgroup barrier per tile. LDS fragment
+// V^T comes from the gfx950 transposed LDS read. K/V tiles go straight from
+// global memory into a two-stage LDS ring (direct-to-LDS loads, swizzled on
+// the global side, conflict-free): tile jt + 1 is in flight while tile jt is
+// computed; one workgroup barrier per tile. LDS fragment
 // reads run a few k-steps ahead of the MFMAs that consume them. The softmax
 // scale folds into the exponent's FMA; the running max used for the exponent
 // is only raised when a row's max grows by more than 2^8, so the O accumulator
@@ -39,6 +39,15 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base must be the same for the whole wave). Completion
+// is counted by vmcnt like any vector-memory load.
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
 // s_waitcnt vmcnt(0) with the other counters untouched (gfx9 encoding).
@@ -69,7 +78,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
                                              int qt) {
   using C = PrefillCfg<D>;
   constexpr int RB = C::RB, BN = C::BN, CPR = C::CPR, KS = C::KS, DBLK = C::DBLK;
-  constexpr int NSTAGE = C::NSTAGE;
   if (b < 0 || b >= a.B || qt >= a.n_qtiles) return;
   const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
   const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
@@ -116,41 +124,30 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + hk * D;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // Tiles reach LDS through registers: the loads of tile jt + 2 are issued
-  // in iteration jt and written to the ring (stage (jt + 2) % NSTAGE,
-  // swizzled) at the start of iteration jt + 1. Thread t moves chunks
-  // t, t + THREADS, ... of the tile (16 bytes each).
+  // Tiles go straight from global memory into a two-stage LDS ring (16
+  // bytes per lane; lane l of a wave lands at the wave's base + 16 l), the
+  // swizzle applied on the global side: the lane that fills slot (row r,
+  // position c') loads chunk swz(r, c') of the row (each swizzle is an XOR,
+  // its own inverse). Tile jt + 1 is issued at the start of iteration jt,
+  // into the stage that tile jt - 1 used.
   constexpr int CH = (BN * CPR + C::THREADS - 1) / C::THREADS;  // chunks per thread (K or V)
-  u32x4 stk[CH], stv[CH];
-  auto load_tile = [&](int jt) {
+  auto issue_tile = [&](int jt, uint8_t* dst) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
-      const int r = q / CPR, c = q % CPR;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;  // whole waves
+      const int r = q / CPR, cp = q % CPR;
       const int64_t key = min(jt * BN + r, kend - 1);
-      stk[i] = ld16(kbase + key * krs + 8 * c);
-      stv[i] = ld16(vbase + key * vrs + 8 * c);
-    }
-  };
-  auto store_tile = [&](int jt) {
-    uint8_t* sk_ = lds + (jt % NSTAGE) * 2 * C::TILE_BYTES;
-    uint8_t* sv_ = sk_ + C::TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
-      const int r = q / CPR, c = q % CPR;
-      *reinterpret_cast<u32x4*>(sk_ + r * D * 2 + swz_rows<D>(r, c) * 16) = stk[i];
-      *reinterpret_cast<u32x4*>(sv_ + r * D * 2 + swz_tr32<D>(r, c) * 16) = stv[i];
+      uint8_t* base = dst + (q - lane) * 16;
+      lds_dma16(kbase + key * krs + 8 * swz_rows<D>(r, cp), base);
+      lds_dma16(vbase + key * vrs + 8 * swz_tr32<D>(r, cp), base + C::TILE_BYTES);
     }
   };
 
   // Tile 0's loads share the Q loads' round trip. Q must be in registers
   // before the loop: an explicit wait here tells the compiler's counter
-  // tracking so, and the loop's MFMAs then never wait on the tile prefetches
-  // issued inside the loop.
-  if (ntiles > 0) load_tile(0);
+  // tracking so.
+  if (ntiles > 0) issue_tile(0, lds);
   wait_vmem_all();
 
   float m[RB], l[RB];
@@ -165,14 +162,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
       for (int j = 0; j < 16; ++j) o[rb][i][j] = 0.f;
   }
 
-  if (ntiles > 0) store_tile(0);
-  if (ntiles > 1) load_tile(1);
-
   // The two halves of tile jt: h1 = S^T = K Q^T + online softmax (leaves
   // bf16 P in pk), h2 = O^T += V^T P^T.
   u32x4 pk[RB][2][2];
-  auto h1 = [&](int jt) {
-    const uint8_t* lk = lds + (jt % NSTAGE) * 2 * C::TILE_BYTES;
+  auto h1 = [&](int jt, const uint8_t* lk) {
     const int key0 = jt * BN;
     // ---- S^T = K Q^T: two 32-key blocks x RB row blocks (K read once)
     f32x16 sacc[RB][2];
@@ -261,8 +254,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
     }
 
   };
-  auto h2 = [&](int jt) {
-    const uint8_t* lv = lds + (jt % NSTAGE) * 2 * C::TILE_BYTES + C::TILE_BYTES;
+  auto h2 = [&](const uint8_t* lv) {
     // ---- O^T += V^T P^T: k-steps (kb, h) of 16 keys; V^T read once for all
     //      row blocks
     // V^T fragments for the 4 k-steps (kb, h) stream from LDS one k-step
@@ -298,17 +290,22 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
     }
   };
 
-  // Ring use: at the start of iteration jt (after the barrier) tile jt + 1
-  // is written into the stage tile jt - 1 used, whose readers all passed the
-  // barrier, and the global loads of tile jt + 2 are issued.
+  // One tile: issue tile jt + 1 into the other stage, then compute tile jt.
+  // The stages are disjoint (restrict), which lets the compiler read `cur`
+  // while the direct loads into `nxt` are in flight.
+  auto tile = [&](int jt, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+    if (jt + 1 < ntiles) issue_tile(jt + 1, nxt);
+    h1(jt, cur);
+    h2(cur + C::TILE_BYTES);
+  };
+  // The barrier also waits for this wave's loads of tile jt (the compiler
+  // completes direct-to-LDS loads before a workgroup barrier), so after it
+  // every wave's part of tile jt is in LDS and no wave still reads the stage
+  // that tile jt + 1 goes to.
   for (int jt = 0; jt < ntiles; ++jt) {
+    wait_vmem_all();
     __syncthreads();
-    if (jt + 1 < ntiles) {
-      store_tile(jt + 1);
-      if (jt + 2 < ntiles) load_tile(jt + 2);
-    }
-    h1(jt);
-    h2(jt);
+    tile(jt, lds + (jt & 1) * 2 * C::TILE_BYTES, lds + ((jt + 1) & 1) * 2 * C::TILE_BYTES);
   }
 
   // ---- epilogue: lane holds O^T[d = 32 db + 8 (i/4) + 4 (lane>>5) + i%4][row]
