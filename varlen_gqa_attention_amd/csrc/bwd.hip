@@ -30,8 +30,10 @@
 //    of its output (recomputing S and dP over the full D), the dq kernel runs
 //    4 waves and the dk/dv kernel steps over 32 rows, to fit the registers.
 // Every contraction is v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
-// dS are rounded to bf16 as MFMA operands. Tiles reach a two-stage LDS ring
-// through registers (loads two steps ahead, one barrier per step).
+// dS are rounded to bf16 as MFMA operands. Tiles pass through a two-stage
+// LDS ring with one barrier per step: the dq kernel's K/V tiles through
+// registers (loads two steps ahead), the dk/dv kernel's Q/dO tiles by
+// direct-to-LDS loads (one step ahead; measured equal in the dq kernel).
 #include <hip/hip_ext.h>
 
 #include "device.hpp"
