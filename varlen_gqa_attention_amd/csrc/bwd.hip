@@ -390,30 +390,40 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   // one step later, so their latency is not waited on at issue.
   float st_lse = 0.f, st_dl = 0.f;
   bool st_dead = false;
-  auto issue_step = [&](int it, uint8_t* dst) {
+  // Per-step addressing (uniform), then the loads in parts: part i = chunk i
+  // of the Q and dO tiles, spread over the step's first MFMA region.
+  const uint16_t* st_qb = a.q;
+  const uint16_t* st_db = a.dout;
+  int st_rlim = 0;
+  auto issue_begin = [&](int it) {
     const int tb = it / a.G, hq = hk * a.G + it % a.G;
     const int tbase = t_first + tb * BN;
     const int rlim = Lq - 1 - tbase;
     const int64_t t0 = (int64_t)sq.start + tbase;
-    const uint16_t* qb = a.q + t0 * a.q_rs + hq * D;
-    const uint16_t* db = a.dout + t0 * a.do_rs + hq * D;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;  // whole waves
-      const int r = q / CPR;
-      const uint32_t rr = (uint32_t)min(r, rlim);
-      const uint32_t c8 = 8 * swz_dual<D>(r, q % CPR);
-      uint8_t* base = dst + (q - lane) * 16;
-      lds_dma16(qb + (__umul24(rr, (uint32_t)a.q_rs) + c8), base);
-      lds_dma16(db + (__umul24(rr, (uint32_t)a.do_rs) + c8), base + TILE);
-    }
+    st_qb = a.q + t0 * a.q_rs + hq * D;
+    st_db = a.dout + t0 * a.do_rs + hq * D;
+    st_rlim = rlim;
     if (threadIdx.x < BN) {
       const uint32_t rr = (uint32_t)min((int)threadIdx.x, rlim);
       st_dead = (int)threadIdx.x > rlim;
       st_lse = a.lse[t0 * a.Hq + hq + __umul24(rr, (uint32_t)a.Hq)];
       st_dl = a.delta[((int64_t)b * a.s_max_q + tbase) * a.Hq + hq + __umul24(rr, (uint32_t)a.Hq)];
     }
+  };
+  auto issue_part = [&](int i, uint8_t* dst) {
+    const int q = threadIdx.x + i * C::THREADS;
+    if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) return;  // whole waves
+    const int r = q / CPR;
+    const uint32_t rr = (uint32_t)min(r, st_rlim);
+    const uint32_t c8 = 8 * swz_dual<D>(r, q % CPR);
+    uint8_t* base = dst + (q - lane) * 16;
+    lds_dma16(st_qb + (__umul24(rr, (uint32_t)a.q_rs) + c8), base);
+    lds_dma16(st_db + (__umul24(rr, (uint32_t)a.do_rs) + c8), base + TILE);
+  };
+  auto issue_step = [&](int it, uint8_t* dst) {
+    issue_begin(it);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) issue_part(i, dst);
   };
   auto put_rows = [&](uint8_t* dst) {
     if (threadIdx.x < BN) {
@@ -434,7 +444,8 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   // from this one. The two stages are disjoint (restrict), which lets the
   // compiler read `lq` while the direct loads into `nxt` are in flight.
   auto step = [&](int it, const uint8_t* __restrict__ lq, uint8_t* __restrict__ nxt) {
-    if (it + 1 < n_it) issue_step(it + 1, nxt);
+    const bool more = it + 1 < n_it;
+    if (more) issue_begin(it + 1);
     const uint8_t* ldo = lq + TILE;
     const float* lrow = reinterpret_cast<const float*>(lq + 2 * TILE);
     const int tbase = t_first + (it / a.G) * BN;
@@ -514,6 +525,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
         else rd(1, ks + PF - KS);
         __builtin_amdgcn_sched_barrier(0);
         mm(0, ks);
+        if (ks < CH && more) issue_part(ks, nxt);
         __builtin_amdgcn_sched_barrier(0);
       }
       // B: two entries of rows 0-31 per k-step of rows 32-63 (the order of
@@ -559,6 +571,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
         if (ks + PF < KS) rd(0, ks + PF);
         __builtin_amdgcn_sched_barrier(0);
         mm(0, ks);
+        if (ks < CH && more) issue_part(ks, nxt);
         __builtin_amdgcn_sched_barrier(0);
       }
       rdt(0);
