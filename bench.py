@@ -240,6 +240,41 @@ def long_decode(args):
     return res, state
 
 
+def shard_decode_measure(args, reps=10):
+    """One GPU's share of the long decode under KV-head sharding over 8 GPUs
+    (B=1, Hq=8, Hkv=1, D=128, Lk=32768): graph-replayed step time with the
+    default plan (split cap 32 and 1024-key minimum chunk: 32 workgroups) and
+    with the split count forced so that the grid fills the CUs."""
+    torch = _torch()
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    B, Hq, Hkv, D, L = 1, 8, 1, 128, 32768
+    kv_bytes = 2 * L * Hkv * D * 2
+    ncopy = max(1, -(-MALL_DEFEAT_BYTES // kv_bytes))
+    q = I.normal_bf16((B, Hq, D), 20, "cuda")
+    ks = [I.normal_bf16((L, Hkv, D), 21 + 2 * i, "cuda") for i in range(ncopy)]
+    vs = [I.normal_bf16((L, Hkv, D), 22 + 2 * i, "cuda") for i in range(ncopy)]
+    cu_q = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    cu_kv = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device="cuda")
+    res = dict(workload=f"one GPU's share of the long decode at 8-way head sharding: B=1, "
+                        f"Hq=8, Hkv=1, D=128, Lk=32768, {ncopy} rotating K/V copies, graphs of "
+                        f"{ncopy} steps", kv_bytes_per_step=kv_bytes)
+    for name, opts in (("default_plan", {}), ("forced_128_splits", dict(force_nsplit=128)),
+                       ("forced_256_splits", dict(force_nsplit=256))):
+        plan = V.Plan(B, 1, L, Hq, Hkv, D, False, **opts)
+        fns = [lambda k=k, v=v: plan(q, k, v, cu_q, cu_kv, out=out, lse=lse, B=B)
+               for k, v in zip(ks, vs)]
+        group = capture(lambda: [f() for f in fns])
+        total, _ = time_replays([group.replay], reps, 2)
+        us = total / (reps * ncopy) * 1e3
+        res[name] = dict(nsplit=plan.info["nsplit"], grid=plan.info["grid"],
+                         us_per_step=round(us, 2),
+                         kv_gbs=round(kv_bytes / (us * 1e-6) / 1e9, 1))
+    return res
+
+
 def cpu_baseline_long_decode(state, budget_s):
     import numpy as np
     from oracle import attention as A
@@ -582,7 +617,7 @@ def main():
                     help="long decode: steps per captured graph (0 = one per K/V copy)")
     ap.add_argument("--workload", default="long_decode",
                     choices=["long_decode", "prefill", "batched_decode", "gathered_decode",
-                             "backward"],
+                             "backward", "shard_decode"],
                     help="headline workload (default: long decode); the others are for "
                          "profiling runs")
     args = ap.parse_args()
@@ -605,8 +640,8 @@ def main():
                           **gathered_measure(**{k: v for k, v in args.plan_opts.items() if v})}))
         return
     if args.workload != "long_decode":
-        fn = {"prefill": prefill_measure, "backward": backward_measure}.get(
-            args.workload, batched_decode_measure)
+        fn = {"prefill": prefill_measure, "backward": backward_measure,
+              "shard_decode": shard_decode_measure}.get(args.workload, batched_decode_measure)
         print(json.dumps({"workload": args.workload, **fn(args)}))
         return
     res, state = long_decode(args)
@@ -620,6 +655,7 @@ def main():
         line["batched_decode"] = batched_decode_measure(args)
         line["gathered_decode"] = gathered_measure()
         line["backward"] = backward_measure(args)
+        line["shard_decode"] = shard_decode_measure(args)
         line["padding_mask"] = mask_measure()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)

@@ -118,6 +118,16 @@ def test_long_decode_full_size():
     assert r["info"]["nsplit"] == 32 and r["info"]["grid"] == 256
 
 
+def test_one_gpu_share_of_long_decode_with_forced_splits():
+    # the head-sharded long decode on one of 8 GPUs (Hq=8, Hkv=1), default
+    # plan and the split count the grid needs to fill the CUs
+    w = _w("shard", 1, 8, 1, 128, [32768])
+    r = run_decode(w, 5)
+    assert r["info"]["nsplit"] == 32 and r["info"]["grid"] == 32
+    r = run_decode(w, 6, force_nsplit=256)
+    assert r["info"]["nsplit"] == 256 and r["info"]["grid"] == 256
+
+
 def test_batched_decode_full_size():
     # 512 (sequence, kv head) units at 8 workgroups per CU: 4 splits, MFMA path
     r = run_decode(I.batched_decode_step(0), 0)
