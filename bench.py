@@ -275,6 +275,38 @@ def shard_decode_measure(args, reps=10):
     return res
 
 
+def small_configs_measure(reps=200):
+    """The two remaining decode configurations, graph-replayed: the tiny
+    decode (B=2, Hq=4, Hkv=1, D=64, KV lengths U[1,128] seed (0,0)), which is
+    latency-bound and reported in µs/step, and the edge sweep (B=33 of
+    B_max=64, Hq=128, Hkv=8, lengths 0..16384, adversarial cu tails) at
+    D = 32, 64 and 256, in µs/step and GB/s of K+V read."""
+    torch = _torch()
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import inputs as I
+    res = {}
+    for w in [I.tiny_decode(0)] + [I.edge_sweep(D) for D in (32, 64, 256)]:
+        m = I.materialise(w, 0, "cuda")
+        plan = V.Plan(w["B_max"], 1, w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], False)
+        out = torch.empty_like(m["q"])
+        lse = torch.empty(m["q"].shape[:2], device="cuda")
+        f = lambda: plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], out=out, lse=lse,
+                         B=w["B"])
+        per_graph = 10   # steps per graph, so that host graph launches stay off the clock
+        g = capture(lambda: [f() for _ in range(per_graph)])
+        total, _ = time_replays([g.replay], reps // per_graph, 2)
+        us = total / (reps // per_graph * per_graph) * 1e3
+        kv = int(2 * w["kv_lens"].sum() * w["Hkv"] * w["D"] * 2)
+        res[w["name"]] = dict(us_per_step=round(us, 2), kv_bytes=kv,
+                              kv_gbs=round(kv / (us * 1e-6) / 1e9, 1),
+                              nsplit=plan.info["nsplit"], grid=plan.info["grid"],
+                              decode_path=("mfma" if plan.info["decode_path"] == 2 else "wave"))
+        plan.close()
+    res["note"] = ("graphs of 10 steps on resident K/V (the edge sweep's K/V fit in the 256 MB "
+                   "Infinity Cache at D = 32 and 64, so those rates are cache-assisted)")
+    return res
+
+
 def cpu_baseline_long_decode(state, budget_s):
     import numpy as np
     from oracle import attention as A
@@ -617,7 +649,7 @@ def main():
                     help="long decode: steps per captured graph (0 = one per K/V copy)")
     ap.add_argument("--workload", default="long_decode",
                     choices=["long_decode", "prefill", "batched_decode", "gathered_decode",
-                             "backward", "shard_decode"],
+                             "backward", "shard_decode", "small_configs"],
                     help="headline workload (default: long decode); the others are for "
                          "profiling runs")
     args = ap.parse_args()
@@ -641,7 +673,9 @@ def main():
         return
     if args.workload != "long_decode":
         fn = {"prefill": prefill_measure, "backward": backward_measure,
-              "shard_decode": shard_decode_measure}.get(args.workload, batched_decode_measure)
+              "shard_decode": shard_decode_measure,
+              "small_configs": lambda _args: small_configs_measure()}.get(
+                  args.workload, batched_decode_measure)
         print(json.dumps({"workload": args.workload, **fn(args)}))
         return
     res, state = long_decode(args)
@@ -656,6 +690,7 @@ def main():
         line["gathered_decode"] = gathered_measure()
         line["backward"] = backward_measure(args)
         line["shard_decode"] = shard_decode_measure(args)
+        line["small_configs"] = small_configs_measure()
         line["padding_mask"] = mask_measure()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)
