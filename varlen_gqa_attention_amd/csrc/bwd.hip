@@ -440,9 +440,11 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
 #pragma unroll
     for (int j = 0; j < 16; ++j) dk[i][j] = dv[i][j] = 0.f;
 
-  // One step: issue the next step's loads into the other stage, then compute
-  // from this one. The two stages are disjoint (restrict), which lets the
-  // compiler read `lq` while the direct loads into `nxt` are in flight.
+  // One step: compute from stage `lq` while the next step's tile loads go to
+  // stage `nxt` (its lse / delta loads first, its tile loads spread between
+  // the first region's MFMAs). The two stages are disjoint (restrict), which
+  // lets the compiler read `lq` while the direct loads into `nxt` are in
+  // flight.
   auto step = [&](int it, const uint8_t* __restrict__ lq, uint8_t* __restrict__ nxt) {
     const bool more = it + 1 < n_it;
     if (more) issue_begin(it + 1);
