@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define VATTN_ABI_VERSION 3
+#define VATTN_ABI_VERSION 4
 
 typedef void* vattn_stream_t; /* a hipStream_t */
 
@@ -88,9 +88,28 @@ typedef struct vattn_plan_s* vattn_plan_t;
  * ablations; nothing is read from the environment on the hot path (the split
  * target that the split-K blog post reads from an environment variable is a
  * plan option here).
+ *
+ * Decode split rule (split-K blog post, The Thinking Process; AstrAI commit
+ * log, split-KV commit): with n_units = B_max * Hkv * head_blocks and
+ * n_tiles = ceil(s_max_kv / 64),
+ *   nsplit = min(ceil(target_blocks_per_cu * n_cu / n_units), n_tiles,
+ *                nsplit_cap, ceil(n_tiles / min_chunk_tiles)),
+ * then chunk_tiles = ceil(n_tiles / nsplit), nsplit = ceil(n_tiles /
+ * chunk_tiles), and a direct write (no combine) iff nsplit == 1.
+ *   - The pages' rule (aim for roughly two workgroups per compute unit, cap
+ *     by the tile count and by 32, and write directly once the batch's KV
+ *     heads alone fill the device): target_blocks_per_cu = 2,
+ *     min_chunk_tiles = 1 (VATTN_PAGES_TARGET, VATTN_PAGES_MIN_CHUNK).
+ *   - The default (all fields 0): target_blocks_per_cu = 8,
+ *     min_chunk_tiles = 16 (measured faster on this chip: finer splits even
+ *     out batches of unequal lengths, and a split keeps at least 1024 keys).
  */
+#define VATTN_DEFAULT_TARGET 8
+#define VATTN_DEFAULT_MIN_CHUNK 16
+#define VATTN_PAGES_TARGET 2
+#define VATTN_PAGES_MIN_CHUNK 1
 typedef struct {
-  int target_blocks_per_cu; /* default 8 */
+  int target_blocks_per_cu; /* 0 = VATTN_DEFAULT_TARGET (8); the pages' rule: 2 */
   int nsplit_cap;           /* default 32 */
   int force_nsplit;         /* > 0: use this split count (capped by the tile count) */
   int force_decode_path;    /* VATTN_DECODE_* */
@@ -103,6 +122,9 @@ typedef struct {
   int backward;             /* 1: also size the plan for vattn_backward (allocates the
                                row-wise <dO, O> buffer, B_max * s_max_q * Hq floats);
                                G <= 256, and G <= 128 at D = 256 */
+  int min_chunk_tiles;      /* fewest 64-key tiles per split at s_max_kv: 0 =
+                               VATTN_DEFAULT_MIN_CHUNK (16); 1 = no floor (the pages'
+                               rule) */
 } vattn_plan_opts;
 
 typedef struct {

@@ -1,9 +1,13 @@
 """Comparison helpers for HIP-vs-oracle parity tests (no attention arithmetic).
 
 Tolerances: bf16 outputs within max |err| <= 1e-2 of the unrounded fp64
-oracle, widened to one bf16 ulp of the reference where that is larger (from
-|O| >= 2, where the ulp is 2^-6; only very short KV reaches such values); fp32 LSE within 1e-3 relative
-(|d| <= 1e-3 * max(1, |LSE|), since LSE can sit near 0); -inf must match
+oracle; only where |O_ref| >= 4, whose bf16 spacing (2^-5) makes a correctly
+rounded value up to 2^-6 > 1e-2 away, the bound is one bf16 ulp of the
+reference (only very short KV reaches such values). fp32 LSE within 1e-3
+relative, |d| <= max(1e-3 |LSE_ref|, 1e-4): the absolute floor covers LSE
+values near 0 (one key whose score is near 0), where the fp32 rounding of the
+D-term score sum (about 2^-24 sqrt(D) sum|q_d k_d| scale, ~1e-5 for N(0, 1)
+inputs at D <= 256) is not relative to the tiny result. -inf must match
 exactly and NaN always fails.
 
 Gradients (bf16 dq, dk, dv) against the unrounded fp64 oracle: every element
@@ -22,7 +26,9 @@ while the Frobenius ratio does not grow with G.
 import numpy as np
 
 OUT_ATOL = 1e-2
+OUT_ULP_FROM = 4.0     # |O_ref| from which one bf16 ulp (2^-5 and up) is the bound
 LSE_RTOL = 1e-3
+LSE_ATOL = 1e-4
 GRAD_ATOL = 2e-2
 GRAD_RTOL = 2.0 ** -8
 GRAD_FRO = 1e-2
@@ -39,7 +45,7 @@ def assert_out_close(got, ref, what=""):
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert not np.isnan(got).any(), f"{what}: NaN in output"
-    tol = np.maximum(OUT_ATOL, bf16_ulp(ref))
+    tol = np.where(np.abs(ref) >= OUT_ULP_FROM, np.maximum(OUT_ATOL, bf16_ulp(ref)), OUT_ATOL)
     err = np.abs(got - ref)
     bad = err > tol
     if bad.any():
@@ -58,7 +64,7 @@ def assert_lse_close(got, ref, what=""):
     assert np.array_equal(np.isneginf(got), ninf), f"{what}: -inf pattern differs"
     g, r = got[~ninf], ref[~ninf]
     err = np.abs(g - r)
-    tol = LSE_RTOL * np.maximum(1.0, np.abs(r))
+    tol = np.maximum(LSE_RTOL * np.abs(r), LSE_ATOL)
     bad = err > tol
     assert not bad.any(), f"{what}: {bad.sum()} LSE values out of tolerance, max err {err.max():.3e}"
     return float(err.max()) if err.size else 0.0

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
                          capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (vattn_\w+)", out))
     assert set(declared_functions()) <= exported
-    assert L.vattn_abi_version() == 3
+    assert L.vattn_abi_version() == 4
 
 
 SWEEP = [(B, S, Hq, Hkv) for B in (1, 2, 33, 64, 300) for S in (1, 100, 4096, 32768)
@@ -68,6 +68,52 @@ def test_describe_equals_oracle_rule(B, S, Hq, Hkv, n_cu):
     assert d["n_qtiles"] == g["n_qtiles"]
     assert d["prefill_persistent"] == 1 and d["grid"] == n_cu
     assert d["scratch_bytes"] == 512 + 4 * B * g["n_qtiles"]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv", SWEEP)
+@pytest.mark.parametrize("n_cu", [256, 80])
+def test_describe_pages_rule_equals_oracle_default(B, S, Hq, Hkv, n_cu):
+    """The pages' split rule (target 2 workgroups per CU, no work floor) is
+    selectable through the plan options, and the library's chooser then equals
+    the oracle's chooser at its defaults, bit for bit."""
+    import varlen_gqa_attention_amd as V
+    _lib()
+    info = V.describe_plan(B, 1, S, Hq, Hkv, 128, 0, n_cu_override=n_cu,
+                           target_blocks_per_cu=2, min_chunk_tiles=1)
+    units = Hkv * info["head_blocks"]
+    want = choose_decode_split(B, S, units, n_cu, info["block_n"])
+    for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
+        assert info[key] == int(want[key]), key
+    assert info["combine_grid"] == (0 if want["direct"] else B * Hq)
+    same = V.describe_plan(B, 1, S, Hq, Hkv, 128, 0, n_cu_override=n_cu, split_rule="pages")
+    assert same == info
+
+
+@pytest.mark.parametrize("T,F", [(1, 1), (2, 16), (4, 4), (8, 1), (16, 8), (3, 2)])
+@pytest.mark.parametrize("B,S,Hq,Hkv", SWEEP[::4])
+def test_describe_any_target_and_floor_equals_oracle(T, F, B, S, Hq, Hkv):
+    import varlen_gqa_attention_amd as V
+    _lib()
+    info = V.describe_plan(B, 1, S, Hq, Hkv, 64, 0, n_cu_override=256,
+                           target_blocks_per_cu=T, min_chunk_tiles=F)
+    want = choose_decode_split(B, S, Hkv * info["head_blocks"], 256, info["block_n"],
+                               target_blocks_per_cu=T, min_chunk_tiles=F)
+    for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
+        assert info[key] == int(want[key]), key
+
+
+def test_default_rule_constants():
+    """All-zero options select the documented default (8 per CU, 16 tiles)."""
+    import varlen_gqa_attention_amd as V
+    _lib()
+    for B, S in ((1, 32768), (64, 8192), (16, 2048), (2, 128), (33, 16384)):
+        a = V.describe_plan(B, 1, S, 32, 8, 128, 0, n_cu_override=256)
+        b = V.describe_plan(B, 1, S, 32, 8, 128, 0, n_cu_override=256,
+                            target_blocks_per_cu=8, min_chunk_tiles=16)
+        assert a == b
+    with pytest.raises(ValueError):
+        V.describe_plan(1, 1, 64, 8, 8, 64, 0, n_cu_override=256, split_rule="pages",
+                        target_blocks_per_cu=2)
 
 
 @pytest.mark.parametrize("force", [1, 2, 3, 7, 32, 100])

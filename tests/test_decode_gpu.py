@@ -70,6 +70,50 @@ def test_tiny_decode_default_plan(seed):
     assert r["err_word"] == 0
 
 
+def _pages_rule_plan_matches_oracle(w, info):
+    """The plan the library chose under the pages' split rule equals the
+    oracle chooser's default (pages') rule."""
+    want = choose_decode_split(w["B_max"], w["s_max_kv"], w["Hkv"] * info["head_blocks"],
+                               info["n_cu"], info["block_n"])
+    assert (info["nsplit"], info["chunk_keys"], info["direct"], info["grid"]) == \
+        (want["nsplit"], want["chunk_keys"], want["direct"], want["grid"])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_decode_pages_rule(seed):
+    """Tiny decode under the pages' rule: the tile count (2 tiles of 64 keys)
+    binds, so two splits and the LSE combine."""
+    w = I.tiny_decode(seed)
+    r = run_decode(w, seed, split_rule="pages")
+    _pages_rule_plan_matches_oracle(w, r["info"])
+    assert r["info"]["nsplit"] == 2 and r["info"]["combine_grid"] > 0
+    assert r["err_word"] == 0
+
+
+def test_long_decode_pages_rule():
+    w = I.long_decode()
+    r = run_decode(w, 3, split_rule="pages")
+    _pages_rule_plan_matches_oracle(w, r["info"])
+    assert r["info"]["nsplit"] == 32
+
+
+def test_batched_decode_full_size_pages_rule():
+    """Continuous batching under the pages' rule: 64 x 8 units fill the
+    device, so one direct-write pass and no combine."""
+    w = I.batched_decode_step(2)
+    r = run_decode(w, 2, split_rule="pages")
+    _pages_rule_plan_matches_oracle(w, r["info"])
+    assert r["info"]["direct"] and r["info"]["combine_grid"] == 0
+
+
+@pytest.mark.parametrize("D", [32, 64, 256])
+def test_edge_sweep_pages_rule(D):
+    w = I.edge_sweep(D)
+    r = run_decode(w, D, split_rule="pages")
+    _pages_rule_plan_matches_oracle(w, r["info"])
+    assert r["info"]["direct"] and r["err_word"] == 0
+
+
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("nsplit", [1, 2])
 def test_tiny_decode_paths(path, nsplit):

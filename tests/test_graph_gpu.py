@@ -70,3 +70,75 @@ def test_graph_replay_with_changing_lengths(nsplit, fuse):
                                           B, False)
         assert_out_close(I.bf16_to_f64(outs[t]), ref_o, f"step {t}")
         assert_lse_close(lses[t].cpu().numpy(), ref_l, f"step {t}")
+
+
+@pytest.mark.timeout(400)
+def test_continuous_batching_full_size_graph_replay():
+    """The continuous-batching workload at its own size: B=64, Hq=32, Hkv=8,
+    D=128, one plan with s_max_kv=8192, one capture of {select this step's
+    cu_seqlens on the device, execute, keep the sampled steps' results},
+    replayed 100 times with lengths U[128, 8192] per step (seed (2, t)). Steps
+    0, 1, 50 and 99 are checked against the oracle and, bit for bit, against
+    an eager execute of the same step."""
+    import varlen_gqa_attention_amd as V
+    steps, sampled = 100, (0, 1, 50, 99)
+    ws = [I.batched_decode_step(t) for t in range(steps)]
+    B, Hq, Hkv, D, smax = 64, 32, 8, 128, 8192
+    cu_steps = torch.from_numpy(np.stack([I.cu_from_lengths(w["kv_lens"]) for w in ws])).cuda()
+    pool = B * smax
+    q = I.normal_bf16((B, Hq, D), 120, "cuda")
+    k = I.normal_bf16((pool, Hkv, D), 121, "cuda")
+    v = I.normal_bf16((pool, Hkv, D), 122, "cuda")
+    cu_q = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    live = torch.zeros(1, B + 1, dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = torch.zeros_like(q)
+    lse = torch.zeros(B, Hq, device="cuda")
+    # slot of each step in the kept results: sampled steps 0..3, the rest 4
+    slot_of = torch.full((steps,), len(sampled), dtype=torch.int64)
+    for i, t in enumerate(sampled):
+        slot_of[t] = i
+    slot_of = slot_of.cuda()
+    slot = torch.zeros(1, dtype=torch.int64, device="cuda")
+    outs = torch.zeros(len(sampled) + 1, B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lses = torch.zeros(len(sampled) + 1, B, Hq, device="cuda")
+    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False)
+    print(f"[graph full size] plan {plan.info}", flush=True)
+
+    def one_step():
+        torch.index_select(cu_steps, 0, step, out=live)
+        plan(q, k, v, cu_q, live.view(-1), out=out, lse=lse, B=B)
+        torch.index_select(slot_of, 0, step, out=slot)
+        outs.index_copy_(0, slot, out.unsqueeze(0))
+        lses.index_copy_(0, slot, lse.unsqueeze(0))
+        step.add_(1)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        one_step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="global"):
+        one_step()
+    torch.cuda.synchronize()
+    step.zero_()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    assert int(step.item()) == steps
+    print("[graph full size] 100 replays done", flush=True)
+    rows = int(cu_steps[list(sampled)].max().item())
+    qf, kf, vf = I.bf16_to_f64(q), I.bf16_to_f64(k[:rows]), I.bf16_to_f64(v[:rows])
+    for i, t in enumerate(sampled):
+        cu_t = cu_steps[t].contiguous()
+        o_e, l_e = plan(q, k, v, cu_q, cu_t, B=B)
+        torch.cuda.synchronize()
+        assert torch.equal(o_e.view(torch.int16), outs[i].view(torch.int16)), f"step {t}"
+        assert torch.equal(l_e, lses[i]), f"step {t}"
+        ref_o, ref_l, _ = A.attend_varlen(qf, kf, vf, np.arange(B + 1), cu_t.cpu().numpy(), B,
+                                          False)
+        assert_out_close(I.bf16_to_f64(outs[i]), ref_o, f"step {t}")
+        assert_lse_close(lses[i].cpu().numpy(), ref_l, f"step {t}")
+        print(f"[graph full size] step {t} matches the oracle", flush=True)

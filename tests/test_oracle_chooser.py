@@ -87,3 +87,63 @@ def test_work_floor_per_split():
             n_tiles = -(-S // 64)
             assert 1 <= p["nsplit"] <= max(1, -(-n_tiles // m))
             assert p["chunk_tiles"] * p["nsplit"] >= n_tiles
+
+
+# (target workgroups per CU, work floor in tiles): the pages' rule (2, 1),
+# this library's default (8, 16), and others around them
+RULES = [(2, 1), (8, 16), (1, 1), (4, 4), (8, 1), (2, 16), (16, 8)]
+
+
+def _brute_force_split(B, S, Hkv, n_cu, bn, T, F, cap=32):
+    """The split rule by enumeration: among chunk sizes (in tiles) whose split
+    count stays within the bound min(ceil(T n_cu / units), tiles, cap,
+    ceil(tiles / F)), the smallest chunk; the count is what that chunk needs."""
+    units = B * Hkv
+    tiles = -(-S // bn)
+    bound = max(1, min(-(-T * n_cu // units), tiles, cap, -(-tiles // F)))
+    for ch in range(1, tiles + 1):
+        if -(-tiles // ch) <= bound:
+            return -(-tiles // ch), ch, bound
+    raise AssertionError("unreachable")
+
+
+@pytest.mark.parametrize("T,F", RULES)
+@pytest.mark.parametrize("B,Hkv,S,n_cu,bn", SWEEP[::3])
+def test_split_rule_properties_any_target_and_floor(T, F, B, Hkv, S, n_cu, bn):
+    """The oracle's rule with its two parameters: the split count equals the
+    enumeration above, never exceeds the target, the tile count, 32 or the
+    floor's bound, covers every tile with no empty split at s_max, and writes
+    directly exactly when one split results."""
+    p = choose_decode_split(B, S, Hkv, n_cu, bn, target_blocks_per_cu=T, min_chunk_tiles=F)
+    ns, ch = p["nsplit"], p["chunk_tiles"]
+    want_ns, want_ch, bound = _brute_force_split(B, S, Hkv, n_cu, bn, T, F)
+    assert (ns, ch) == (want_ns, want_ch)
+    tiles = -(-S // bn)
+    assert 1 <= ns <= bound and ns <= 32 and ns <= tiles and ns <= -(-tiles // F)
+    assert (ns - 1) * ch < tiles <= ns * ch
+    assert 2 * ns > bound
+    assert p["direct"] == (ns == 1)
+    if B * Hkv >= T * n_cu:
+        assert p["direct"]      # the batch's units alone fill the target
+    assert p["grid"] == B * Hkv * ns and p["chunk_keys"] == ch * bn
+
+
+def test_split_rule_pages_regimes_of_the_workloads():
+    """The pages' rule (target 2, no floor) on the five workload shapes at
+    64-key tiles and 256 CUs."""
+    # tiny decode: 2 units, 128 keys -> the tile count (2) binds: two splits
+    p = choose_decode_split(2, 128, 1, 256, 64)
+    assert (p["nsplit"], p["chunk_keys"], p["direct"]) == (2, 64, False)
+    # long decode: 8 units -> 64 wanted, the cap binds: 32 splits of 1024 keys
+    p = choose_decode_split(1, 32768, 8, 256, 64)
+    assert (p["nsplit"], p["chunk_keys"], p["grid"]) == (32, 1024, 256)
+    # continuous batching: 64 x 8 = 512 units >= 2 per CU -> direct write
+    p = choose_decode_split(64, 8192, 8, 256, 64)
+    assert p["direct"] and p["grid"] == 512
+    # edge sweep: B_max 64 x 8 units -> direct write
+    p = choose_decode_split(64, 16384, 8, 256, 64)
+    assert p["direct"] and p["grid"] == 512
+    # one GPU's share of the long decode at 8-way head sharding: 1 unit ->
+    # 512 wanted, the cap binds
+    p = choose_decode_split(1, 32768, 1, 256, 64)
+    assert p["nsplit"] == 32 and p["grid"] == 32

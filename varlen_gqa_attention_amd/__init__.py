@@ -33,10 +33,26 @@ __all__ = ["Plan", "padding_mask", "cross_padding_masks", "describe_plan", "Vatt
            "ERRBIT_INDEX"]
 
 
+# Decode split rules (include/vattn.h, vattn_plan_opts): "pages" is the rule
+# the split-K pages state (about two workgroups per CU, no work floor);
+# "default" is this library's tuned default (8 per CU, 16 tiles per split).
+SPLIT_RULES = {"default": dict(target_blocks_per_cu=0, min_chunk_tiles=0),
+               "pages": dict(target_blocks_per_cu=2, min_chunk_tiles=1)}
+
+
 def _opts(target_blocks_per_cu=0, nsplit_cap=0, force_nsplit=0, force_decode_path=0,
-          n_cu_override=0, fuse_combine=0, decode_waves=0, prefill_grid=0, backward=0):
+          n_cu_override=0, fuse_combine=0, decode_waves=0, prefill_grid=0, backward=0,
+          min_chunk_tiles=0, split_rule=None):
+    if split_rule is not None:
+        if split_rule not in SPLIT_RULES:
+            raise ValueError(f"split_rule must be one of {sorted(SPLIT_RULES)}")
+        if target_blocks_per_cu or min_chunk_tiles:
+            raise ValueError("give split_rule or target_blocks_per_cu / min_chunk_tiles, not both")
+        target_blocks_per_cu = SPLIT_RULES[split_rule]["target_blocks_per_cu"]
+        min_chunk_tiles = SPLIT_RULES[split_rule]["min_chunk_tiles"]
     return PlanOpts(target_blocks_per_cu, nsplit_cap, force_nsplit, force_decode_path,
-                    n_cu_override, fuse_combine, decode_waves, prefill_grid, int(backward))
+                    n_cu_override, fuse_combine, decode_waves, prefill_grid, int(backward),
+                    min_chunk_tiles)
 
 
 def describe_plan(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, **opts):

@@ -35,7 +35,8 @@ EXPORTS = (
 class PlanOpts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "target_blocks_per_cu", "nsplit_cap", "force_nsplit", "force_decode_path",
-        "n_cu_override", "fuse_combine", "decode_waves", "prefill_grid", "backward")]
+        "n_cu_override", "fuse_combine", "decode_waves", "prefill_grid", "backward",
+        "min_chunk_tiles")]
 
 
 _INFO_INT_FIELDS = (

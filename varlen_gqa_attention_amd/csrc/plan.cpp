@@ -14,14 +14,15 @@
 // ceil(target * n_cu / n_units) with n_units the decode workgroups per split;
 // "tile count" is ceil(s_max_kv / 64); splits are contiguous chunks of whole
 // tiles and the count is recomputed from the chunk size so that no split is
-// empty at s_max_kv. The target itself is tuned for this chip: 8 workgroups
+// empty at s_max_kv. The pages' rule is a plan option (target 2 workgroups
+// per CU, no work floor). The default is tuned for this chip: 8 workgroups
 // per CU measured best (a CU holds several decode workgroups at once, and
 // finer splits even out batches whose lengths vary, where the longest
 // sequence's workgroup would otherwise set the step time); the rule's form,
-// caps and direct-write fallback are unchanged. One bound is added: a split
-// keeps at least 16 tiles (1024 keys) at s_max_kv, below which the
-// per-workgroup start and merge cost more than the parallelism returns
-// (measured on 2048-key gathered lists and 8192-key batches).
+// caps and direct-write fallback are unchanged. One bound is added by
+// default: a split keeps at least 16 tiles (1024 keys) at s_max_kv, below
+// which the per-workgroup start and merge cost more than the parallelism
+// returns (measured on 2048-key gathered lists and 8192-key batches).
 #include "plan.hpp"
 
 #include <stdint.h>
@@ -43,6 +44,7 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
   if (opts) o = *opts;
   const int target = o.target_blocks_per_cu > 0 ? o.target_blocks_per_cu : kDecodeTargetPerCu;
   const int cap = o.nsplit_cap > 0 ? o.nsplit_cap : 32;
+  const int min_chunk = o.min_chunk_tiles > 0 ? o.min_chunk_tiles : kMinChunkTiles;
   const int G = Hq / Hkv;
 
   vattn_plan_info in = {};
@@ -76,8 +78,8 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
       int64_t ns = want;
       if (ns > in.n_tiles) ns = in.n_tiles;
       if (ns > cap) ns = cap;
-      // each split keeps at least kMinChunkTiles tiles of work at s_max_kv
-      const int64_t by_work = cdiv(in.n_tiles, kMinChunkTiles);
+      // each split keeps at least min_chunk tiles of work at s_max_kv
+      const int64_t by_work = cdiv(in.n_tiles, min_chunk);
       if (ns > by_work) ns = by_work;
       nsplit = ns < 1 ? 1 : (int)ns;
     }

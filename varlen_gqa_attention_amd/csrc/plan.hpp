@@ -11,8 +11,8 @@ constexpr int kDecodeMfmaHeads = 16;  // heads per workgroup on the MFMA decode 
 constexpr int kDecodeWaveHeads = 4;   // heads per workgroup on the wave decode path
 constexpr int kWaveMaxG = 3;          // auto: G <= this uses the wave path (MFMA measured
                                       // faster from G = 4 on)
-constexpr int kDecodeTargetPerCu = 8;  // split rule: workgroups per CU to aim for
-constexpr int kMinChunkTiles = 16;     // split rule: fewest KV tiles per split
+constexpr int kDecodeTargetPerCu = VATTN_DEFAULT_TARGET;  // split rule: workgroups per CU to aim for
+constexpr int kMinChunkTiles = VATTN_DEFAULT_MIN_CHUNK;   // split rule: fewest KV tiles per split
 // query rows (heads x tokens) per prefill workgroup: 8 waves (4 for D = 256)
 // of 32 rows; threads per prefill workgroup
 constexpr int prefill_rows(int D) { return D <= 128 ? 256 : 128; }

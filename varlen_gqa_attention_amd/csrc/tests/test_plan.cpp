@@ -85,6 +85,39 @@ int main() {
           CHECK(in.direct == (in.nsplit == 1));
           if (in.n_units >= 8 * 256) CHECK(in.direct);
         }
+  {
+    // the pages' rule: about two workgroups per CU, no work floor
+    vattn_plan_opts pg = {};
+    pg.target_blocks_per_cu = VATTN_PAGES_TARGET;
+    pg.min_chunk_tiles = VATTN_PAGES_MIN_CHUNK;
+    // tiny decode (2 units, 2 tiles): two splits and a combine
+    CHECK(vattn::plan_compute(2, 1, 128, 4, 1, 64, 0, &pg, 256, &in) == VATTN_OK);
+    CHECK(in.nsplit == 2 && !in.direct && in.chunk_keys == 64 && in.combine_grid == 2 * 4);
+    // long decode: the cap of 32 binds
+    CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, &pg, 256, &in) == VATTN_OK);
+    CHECK(in.nsplit == 32 && in.grid == 256 && in.chunk_keys == 1024);
+    // continuous batching and the edge sweep: 512 units fill the device
+    CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, &pg, 256, &in) == VATTN_OK);
+    CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0 && in.grid == 512);
+    CHECK(vattn::plan_compute(64, 1, 16384, 128, 8, 256, 0, &pg, 256, &in) == VATTN_OK);
+    CHECK(in.direct && in.grid == 512);
+    // 2048-key lists over 128 units: 4 splits of 512 keys (no floor)
+    CHECK(vattn::plan_compute(16, 1, 2048, 32, 8, 128, 0, &pg, 256, &in) == VATTN_OK);
+    CHECK(in.nsplit == 4 && in.chunk_keys == 512);
+    for (int B : Bs)
+      for (int S : Ss)
+        for (int Hkv : Hs) {
+          CHECK(vattn::plan_compute(B, 1, S, Hkv * 8, Hkv, 64, 0, &pg, 256, &in) == VATTN_OK);
+          const int tiles = cdiv(S, 64);
+          int want = cdiv(2 * 256, in.n_units);
+          if (want > tiles) want = tiles;
+          if (want > 32) want = 32;
+          const int ch = cdiv(tiles, want);
+          CHECK(in.nsplit == cdiv(tiles, ch) && in.chunk_keys == ch * 64);
+          CHECK(in.direct == (in.nsplit == 1));
+          if (in.n_units >= 2 * 256) CHECK(in.direct);
+        }
+  }
   vattn_plan_opts o = {};
   o.force_nsplit = 7;
   CHECK(vattn::plan_compute(1, 1, 64 * 40, 8, 8, 64, 0, &o, 256, &in) == VATTN_OK);
