@@ -12,20 +12,7 @@
 #include "../../include/vattn.h"
 #include "launch.hpp"
 #include "plan.hpp"
-
-struct vattn_plan_s {
-  vattn_plan_info info;
-  int device;
-  uint8_t* scratch;  // error word | merge counters | (m, l) partials | O partials
-  int32_t* err;
-  int32_t* counters;
-  float2* part_ml;
-  float* part_o;
-  int32_t* sched_count;  // prefill schedule: live-tile count, then the list
-  int32_t* sched_list;
-  float* delta;          // backward: [B_max, s_max_q, Hq] row-wise <dout, out>
-  hipEvent_t ev_start, ev_stop;  // measurement hook (caller-owned), or null
-};
+#include "plan_state.hpp"
 
 namespace {
 
@@ -45,6 +32,36 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 inline uintptr_t align_up(uintptr_t x, uintptr_t a) { return (x + a - 1) & ~(a - 1); }
 
 }  // namespace
+
+namespace vattn {
+
+uint64_t scratch_layout(const vattn_plan_info& info, uint8_t* base, vattn_plan_s* p) {
+  const uint64_t n_cnt = info.direct || !info.is_decode ? 0 : (uint64_t)info.n_units;
+  const uint64_t off_cnt = 256;
+  const uint64_t off_ml = align_up(off_cnt + n_cnt * sizeof(int32_t), 256);
+  const uint64_t n_part =
+      info.direct || !info.is_decode ? 0 : (uint64_t)info.B_max * info.Hq * info.nsplit;
+  const uint64_t off_o = align_up(off_ml + n_part * sizeof(float4), 256);
+  uint64_t total = off_o + n_part * (uint64_t)info.D * sizeof(float);
+  if (info.prefill_persistent)
+    total = 512 + (uint64_t)info.B_max * info.n_qtiles * sizeof(int32_t);
+  const uint64_t off_delta = align_up(total, 256);
+  if (info.backward)
+    total = off_delta + (uint64_t)info.B_max * info.s_max_q * info.Hq * sizeof(float);
+  if (base && p) {
+    p->scratch = base;
+    p->err = (int32_t*)base;
+    p->counters = n_cnt ? (int32_t*)(base + off_cnt) : nullptr;
+    p->part_ml = n_part ? (float4*)(base + off_ml) : nullptr;
+    p->part_o = n_part ? (float*)(base + off_o) : nullptr;
+    p->sched_count = info.prefill_persistent ? (int32_t*)(base + 256) : nullptr;
+    p->sched_list = info.prefill_persistent ? (int32_t*)(base + 512) : nullptr;
+    p->delta = info.backward ? (float*)(base + off_delta) : nullptr;
+  }
+  return total;
+}
+
+}  // namespace vattn
 
 extern "C" {
 
@@ -88,20 +105,7 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
   if (!p) return VATTN_ERR_OOM;
   p->info = info;
   p->device = dev;
-  // layout: [0, 256) error word; then for decode merge counters, (m, l)
-  // pairs and O partials; for a scheduled prefill [256, 512) the live-tile
-  // count and from 512 the list (B_max * n_qtiles entries)
-  const uintptr_t n_cnt = info.direct ? 0 : (uintptr_t)info.n_units;
-  const uintptr_t off_cnt = 256;
-  uintptr_t off_ml = align_up(off_cnt + n_cnt * sizeof(int32_t), 256);
-  uintptr_t n_part = info.direct ? 0 : (uintptr_t)B_max * Hq * info.nsplit;
-  uintptr_t off_o = align_up(off_ml + n_part * sizeof(float2), 256);
-  uintptr_t total = off_o + n_part * (uintptr_t)D * sizeof(float);
-  if (info.prefill_persistent)
-    total = 512 + (uintptr_t)B_max * info.n_qtiles * sizeof(int32_t);
-  // backward: the row-wise <dout, out> buffer at the end
-  const uintptr_t off_delta = align_up(total, 256);
-  if (info.backward) total = off_delta + (uintptr_t)B_max * s_max_q * Hq * sizeof(float);
+  const uint64_t total = vattn::scratch_layout(info, nullptr, nullptr);
   p->info.scratch_bytes = (long long)total;
   void* mem = nullptr;
   hipError_t e = hipMalloc(&mem, total);
@@ -110,18 +114,12 @@ vattn_status vattn_plan_ex(vattn_plan_t* out, int B_max, int s_max_q, int s_max_
     delete p;
     return e == hipErrorOutOfMemory ? VATTN_ERR_OOM : VATTN_ERR_HIP;
   }
-  p->scratch = (uint8_t*)mem;
-  p->err = (int32_t*)mem;
-  p->counters = n_cnt ? (int32_t*)(p->scratch + off_cnt) : nullptr;
-  p->part_ml = n_part ? (float2*)(p->scratch + off_ml) : nullptr;
-  p->part_o = n_part ? (float*)(p->scratch + off_o) : nullptr;
-  p->sched_count = info.prefill_persistent ? (int32_t*)(p->scratch + 256) : nullptr;
-  p->sched_list = info.prefill_persistent ? (int32_t*)(p->scratch + 512) : nullptr;
-  p->delta = info.backward ? (float*)(p->scratch + off_delta) : nullptr;
+  vattn::scratch_layout(info, (uint8_t*)mem, p);
+  const int n_cnt = p->counters ? info.n_units : 0;
   // plan creation may synchronise (it is not on the hot path): zero the
-  // error word once with a kernel, then wait for it.
+  // error word and the merge counters once with kernels, then wait for them.
   if (vattn::launch_clear_word(p->err, nullptr) != hipSuccess ||
-      vattn::launch_clear_words(p->counters, (int)n_cnt, nullptr) != hipSuccess ||
+      vattn::launch_clear_words(p->counters, n_cnt, nullptr) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(mem);
     delete p;
@@ -273,13 +271,24 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
   return e == hipSuccess ? VATTN_OK : VATTN_ERR_HIP;
 }
 
-vattn_status vattn_execute(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
-                           const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
-                           int64_t q_rows, int64_t kv_rows, vattn_stream_t stream) {
+}  // extern "C"
+
+vattn_status vattn::execute_packed(vattn_plan_s* p, int B, const void* q, const void* k,
+                                   const void* v, const int32_t* cu_q, const int32_t* cu_kv,
+                                   void* out, float* lse, int64_t q_rows, int64_t kv_rows,
+                                   vattn_stream_t stream) {
   vattn_status st = check_exec(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows);
   if (st != VATTN_OK || B == 0) return st;
   return run(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, nullptr, 0,
              packed_strides(p->info), stream);
+}
+
+extern "C" {
+
+vattn_status vattn_execute(vattn_plan_t p, int B, const void* q, const void* k, const void* v,
+                           const int32_t* cu_q, const int32_t* cu_kv, void* out, float* lse,
+                           int64_t q_rows, int64_t kv_rows, vattn_stream_t stream) {
+  return vattn::execute_packed(p, B, q, k, v, cu_q, cu_kv, out, lse, q_rows, kv_rows, stream);
 }
 
 vattn_status vattn_execute_gathered(vattn_plan_t p, int B, const void* q, const void* k,

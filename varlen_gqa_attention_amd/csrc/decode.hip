@@ -48,6 +48,8 @@ typedef bf16x2 bf16x2_t;
 // element expression (it reads element 0 whatever the index).
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 
+constexpr uint32_t kBf16One2 = 0x3F803F80u;  // two bf16 ones
+
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
 }
@@ -143,6 +145,10 @@ __device__ __forceinline__ void st_part(float* p, float v) {
 
 // LSE merge of split partials of heads [h0, h0 + nh) of sequence b, written
 // as bf16 out and fp32 LSE; one thread per (head, d), nh * D <= blockDim.x.
+// A partial is (O, m, l, lt): lt sums the weights as they entered the P V
+// product (rounded to bf16 on the MFMA path, equal to l on the wave path);
+// O is normalised by the merged lt, so that the output is a weighted mean of
+// V rows with exactly the weights used, and the LSE is taken from l.
 // Used by the combine kernel and by the fused merge, with the same arithmetic
 // in both. Slots are taken in chunks of 32: lane j of each 32-lane half loads
 // slot s0 + j's (m, l) (a half never spans two heads, since D >= 32), the
@@ -168,11 +174,12 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h
   const int h = idx / D, d = idx % D;
   const int hq = h0 + min(h, nh - 1);
   const int64_t base = (int64_t)(b * a.Hq + hq) * a.nsplit;
-  float ms, ls, po[CH];
+  float ms, ls, lts, po[CH];
   auto load_chunk = [&](int s0, int n_slots) {
     const int64_t si = base + min(s0 + sl, n_slots - 1);
-    ms = ld_part<COHERENT>(pml + 2 * si);
-    ls = ld_part<COHERENT>(pml + 2 * si + 1);
+    ms = ld_part<COHERENT>(pml + 4 * si);
+    ls = ld_part<COHERENT>(pml + 4 * si + 1);
+    lts = ld_part<COHERENT>(pml + 4 * si + 2);
 #pragma unroll
     for (int j = 0; j < CH; ++j)
       po[j] = ld_part<COHERENT>(a.part_o + (base + min(s0 + j, n_slots - 1)) * D + d);
@@ -180,7 +187,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h
   load_chunk(0, a.nsplit);
   const MergeTarget tg = lens();
   if (tg.n_live < 0 || h >= nh) return;  // uniform per 32-lane half
-  float M = kNegInf, L = 0.f, O = 0.f;
+  float M = kNegInf, L = 0.f, Lt = 0.f, O = 0.f;
   for (int s0 = 0; s0 < tg.n_live; s0 += CH) {
     if (s0 > 0) load_chunk(s0, tg.n_live);
     const bool live = s0 + sl < tg.n_live;
@@ -189,6 +196,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h
     const float r = fast_exp2(M - Ms);
     const float wl = live ? fast_exp2(ms - Ms) : 0.f;
     L = L * r + group_sum<32>(live ? wl * ls : 0.f);
+    Lt = Lt * r + group_sum<32>(live ? wl * lts : 0.f);
     O *= r;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -200,23 +208,23 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h
     }
     M = Mn;
   }
-  store_out(a, tg.qrow, hq, d, (L > 0.f) ? O / L : 0.f);
+  store_out(a, tg.qrow, hq, d, (Lt > 0.f) ? O / Lt : 0.f);
   if (d == 0) a.lse[(int64_t)tg.qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 // Cross-wave merge of per-wave (m, l, O) states held in LDS, then the
 // epilogue: direct (normalised bf16 out + LSE) or split partial; in fused
 // mode the last split workgroup of the unit then merges all partials.
-// mo: [NW][HPB][D] floats, mml: [NW][HPB] (m, l) pairs. One thread per
+// mo: [NW][HPB][D] floats, mml: [NW][HPB] (m, l, lt, -). One thread per
 // (head, 4 consecutive d), so LDS reads and global stores are 8-16 bytes.
 template <int D, int NW, int HPB, bool FUSED>
 __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const UnitCoords& u, int Lk,
                                                  int qrow, int h0, int nh, const float* mo,
-                                                 const float2* mml, int* flag) {
+                                                 const float4* mml, int* flag) {
   constexpr int D4 = D / 4;
   for (int idx = threadIdx.x; idx < nh * D4; idx += NW * 64) {
     const int h = idx / D4, d = 4 * (idx % D4);
-    float2 ml[NW];
+    float4 ml[NW];
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -224,17 +232,18 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
       M = fmaxf(M, ml[w].x);
     }
     const float Ms = (M == kNegInf) ? 0.f : M;
-    float L = 0.f;
+    float L = 0.f, Lt = 0.f;
     f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float wt = fast_exp2(ml[w].x - Ms);
       L += wt * ml[w].y;
+      Lt += wt * ml[w].z;
       O += wt * *reinterpret_cast<const f32x4*>(mo + (w * HPB + h) * D + d);
     }
     const int hq = h0 + h;
     if (a.direct) {
-      const float inv = (L > 0.f) ? 1.f / L : 0.f;
+      const float inv = (Lt > 0.f) ? 1.f / Lt : 0.f;
       u32x2 ov;
       ov[0] = pack_bf16x2(O[0] * inv, O[1] * inv);
       ov[1] = pack_bf16x2(O[2] * inv, O[3] * inv);
@@ -248,12 +257,13 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
 #pragma unroll
         for (int i = 0; i < 4; ++i) st_part<true>(a.part_o + pidx * D + d + i, O[i]);
         if (d == 0) {
-          st_part<true>(pml + 2 * pidx, M);
-          st_part<true>(pml + 2 * pidx + 1, L);
+          st_part<true>(pml + 4 * pidx, M);
+          st_part<true>(pml + 4 * pidx + 1, L);
+          st_part<true>(pml + 4 * pidx + 2, Lt);
         }
       } else {
         *reinterpret_cast<f32x4*>(a.part_o + pidx * D + d) = O;
-        if (d == 0) a.part_ml[pidx] = float2{M, L};
+        if (d == 0) a.part_ml[pidx] = float4{M, L, Lt, 0.f};
       }
     }
   }
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int DV = D / 16;     // 16-byte V loads per lane per tile
   constexpr int HPB = 16;        // heads per workgroup
   constexpr int STAGE_BYTES = NW * TILE * D * 2;
-  constexpr int MERGE_BYTES = NW * HPB * D * 4 + 2 * NW * HPB * 4;
+  constexpr int MERGE_BYTES = NW * HPB * D * 4 + 4 * NW * HPB * 4;
   constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int s_flag;
@@ -326,7 +336,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     qv[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
-  float m = kNegInf, l = 0.f;
+  // l: sum of the fp32 weights (for the LSE); lt: sum of the same weights
+  // rounded to bf16 as they enter the P V product (normalises O)
+  float m = kNegInf, l = 0.f, lt = 0.f;
   f32x4 o[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -439,6 +451,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     pw[1] = pack_bf16x2(p[2], p[3]);
     pw[2] = pack_bf16x2(p[4], p[5]);
     pw[3] = pack_bf16x2(p[6], p[7]);
+    float ptsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ptsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[j]), as_bf16x2(kBf16One2), ptsum, false);
+    lt = lt * alpha + ptsum;
     const bf16x8 pt = __builtin_bit_cast(bf16x8, pw);
 
     wave_lds_sync();
@@ -466,14 +483,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   if constexpr (GATHER) report(a.err, gflags);
   // l: each lane summed its own 8 keys per tile; add the four key groups
   l = sum_xor32(sum_xor16(l));
+  lt = sum_xor32(sum_xor16(lt));
 
   __syncthreads();  // staging area becomes the merge area
   float* mo = reinterpret_cast<float*>(lds);
-  float2* mml = reinterpret_cast<float2*>(mo + NW * HPB * D);
+  float4* mml = reinterpret_cast<float4*>(mo + NW * HPB * D);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
     *reinterpret_cast<f32x4*>(mo + (w * HPB + hl) * D + 16 * db + 4 * g4) = o[db];
-  if (g4 == 0) mml[w * HPB + hl] = float2{m, l};
+  if (g4 == 0) mml[w * HPB + hl] = float4{m, l, lt, 0.f};
   __syncthreads();
   finish_workgroup<D, NW, HPB, FUSED>(a, u, Lk, qrow, h0, nh, mo, mml, &s_flag);
 }
@@ -487,7 +505,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   constexpr int RPI = 64 / LPR;          // key rows per load instruction
   constexpr int TILE = (D <= 64) ? 32 : 16;  // keys per wave iteration (two tiles in flight)
   constexpr int NI = TILE / RPI;         // loads per tile for K and for V
-  constexpr int MERGE_FLOATS = NW * GM * D + 2 * NW * GM;
+  constexpr int MERGE_FLOATS = NW * GM * D + 4 * NW * GM;
   __shared__ __attribute__((aligned(16))) float lds[MERGE_FLOATS];
   __shared__ int s_flag;
 
@@ -646,7 +664,7 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) o[g][j] = across_groups_sum<LPR>(o[g][j]);
   }
   float* mo = lds;
-  float2* mml = reinterpret_cast<float2*>(mo + NW * GM * D);
+  float4* mml = reinterpret_cast<float4*>(mo + NW * GM * D);
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
@@ -658,7 +676,8 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < GM; ++g) mml[w * GM + g] = float2{m[g], l[g]};
+    // P V runs in fp32 here: the weights are used unrounded (lt = l)
+    for (int g = 0; g < GM; ++g) mml[w * GM + g] = float4{m[g], l[g], l[g], 0.f};
   }
   __syncthreads();
   finish_workgroup<D, NW, GM, FUSED>(a, u, Lk, qrow, h0, nh, mo, mml, &s_flag);

@@ -14,7 +14,8 @@ struct DecodeArgs {
   uint16_t* out;
   float* lse;
   float* part_o;    // [B_max, Hq, nsplit, D] unnormalised partial outputs
-  float2* part_ml;  // [B_max, Hq, nsplit] (m in log2 units, l)
+  float4* part_ml;  // [B_max, Hq, nsplit] (m in log2 units, l, lt, unused): l sums the
+                    // weights in fp32, lt as they entered P V (bf16 on the MFMA path)
   int32_t* err;
   int32_t* counters;  // [n_units] arrival counters of the fused merge (kept at 0 between launches)
   // Gathered keys (null: contiguous): key j of sequence b is K/V row

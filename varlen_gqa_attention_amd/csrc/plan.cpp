@@ -106,7 +106,7 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     in.scratch_bytes = 256;  // error word, aligned
     if (!in.direct)
       in.scratch_bytes += (int64_t)in.n_units * 4 + 256 +
-                          (int64_t)B_max * Hq * nsplit * ((int64_t)D * 4 + 8) + 256;
+                          (int64_t)B_max * Hq * nsplit * ((int64_t)D * 4 + 16) + 256;
   } else {
     if (G > prefill_rows(D)) return VATTN_ERR_UNSUPPORTED;
     in.q_tokens_per_tile = prefill_rows(D) / G;

@@ -150,12 +150,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   if (ntiles > 0) issue_tile(0, lds);
   wait_vmem_all();
 
-  float m[RB], l[RB];
+  // l: sum of the fp32 weights (for the LSE); lt: sum of the same weights
+  // rounded to bf16 as they enter the P V product (normalises O, so the
+  // output is a weighted mean of V rows with exactly the weights used)
+  float m[RB], l[RB], lt[RB];
   f32x16 o[RB][DBLK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegInf;
     l[rb] = 0.f;
+    lt[rb] = 0.f;
 #pragma unroll
     for (int i = 0; i < DBLK; ++i)
 #pragma unroll
@@ -233,12 +237,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
         if (grow) {
           m[rb] = mnew;
           l[rb] *= alpha;
+          lt[rb] *= alpha;
 #pragma unroll
           for (int i = 0; i < DBLK; ++i) o[rb][i] *= alpha;
         }
       }
       const float msub = (m[rb] == kNegInf) ? 0.f : m[rb];
-      float psum = 0.f;
+      float psum = 0.f, ptsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -248,9 +253,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
             const float p0 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j], a.c, -msub));
             const float p1 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j + 1], a.c, -msub));
             psum += p0 + p1;
-            pk[rb][kb][h][j] = pack_bf16x2(p0, p1);
+            const uint32_t w2 = pack_bf16x2(p0, p1);
+            pk[rb][kb][h][j] = w2;
+            ptsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2),
+                                                    __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                                    ptsum, false);
           }
       l[rb] += psum;
+      lt[rb] += ptsum;
     }
 
   };
@@ -311,9 +321,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   // ---- epilogue: lane holds O^T[d = 32 db + 8 (i/4) + 4 (lane>>5) + i%4][row]
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float lt = sum_xor32(l[rb]);
+    const float ls = sum_xor32(l[rb]), lts = sum_xor32(lt[rb]);
     if (!row_ok[rb]) continue;
-    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+    const float inv = (lts > 0.f) ? 1.f / lts : 0.f;
     uint16_t* op = a.out + (int64_t)(sq.start + tok[rb]) * a.o_rs + hq[rb] * D + 4 * (lane >> 5);
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -326,7 +336,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
       }
     if ((lane >> 5) == 0)
       a.lse[(int64_t)(sq.start + tok[rb]) * a.Hq + hq[rb]] =
-          (lt > 0.f) ? (m[rb] + fast_log2(lt)) * kLn2 : kNegInf;
+          (ls > 0.f) ? (m[rb] + fast_log2(ls)) * kLn2 : kNegInf;
   }
 }
 
