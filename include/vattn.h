@@ -67,7 +67,9 @@ typedef enum {
   VATTN_ERR_INVALID_ARG = -1,  /* bad size, null or misaligned pointer, B > B_max */
   VATTN_ERR_UNSUPPORTED = -2,  /* e.g. D not in {32, 64, 128, 256} */
   VATTN_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
-  VATTN_ERR_OOM = -4           /* plan scratch could not be allocated */
+  VATTN_ERR_OOM = -4,          /* plan scratch could not be allocated */
+  VATTN_ERR_TOO_LARGE = -5     /* vattn_execute_noalloc: the plan's scratch exceeds
+                                  VATTN_NOALLOC_SCRATCH_BYTES */
 } vattn_status;
 
 /* Bits of the device error word (sticky until vattn_plan_clear_error). */
@@ -361,6 +363,35 @@ vattn_status vattn_plan_clear_error(vattn_plan_t p, vattn_stream_t stream);
  * graphs). Host-only call: no device work, no synchronisation.
  */
 vattn_status vattn_plan_set_kernel_events(vattn_plan_t p, void* start, void* stop);
+
+/*
+ * For callers that cannot allocate device memory (code under graph capture
+ * that must not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation): vattn_plan + vattn_execute in one call that allocates
+ * nothing, neither device nor host memory. The plan (B_max, s_max_q, s_max_kv, Hq, Hkv, D,
+ * causal; default options) is chosen on the host at each call exactly as
+ * vattn_plan would choose it, and its scratch (error word, split partials)
+ * lives in a static device array of VATTN_NOALLOC_SCRATCH_BYTES bytes that
+ * each GPU the library runs on holds until the process ends. A plan whose
+ * scratch would not fit returns VATTN_ERR_TOO_LARGE before anything is
+ * enqueued (the split partials take B_max * Hq * nsplit * (4 D + 16) bytes,
+ * plus the merge counters: e.g. B_max = 1, Hq = 64, D = 128 at 32 splits
+ * needs about 1.1 MB). The arguments B .. kv_rows and the results are as
+ * for vattn_execute (packed layouts, same alignment rules, same kernels,
+ * bit-identical results). err_word: an int32 in device memory (4-byte
+ * aligned) into which the kernels OR the VATTN_ERRBIT_* flags, or NULL to
+ * discard them; the caller clears it. All calls on one GPU share that GPU's
+ * array: calls that overlap on a GPU (other streams, other host threads)
+ * race, so serialise them. The first call on a device looks up the array's
+ * device address there (one host-side runtime query, no allocation).
+ */
+#define VATTN_NOALLOC_SCRATCH_BYTES (8u << 20)
+vattn_status vattn_execute_noalloc(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv, int D,
+                                   int causal, int B, const void* q, const void* k,
+                                   const void* v, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv, void* out, float* lse,
+                                   int64_t q_rows, int64_t kv_rows, int32_t* err_word,
+                                   vattn_stream_t stream);
 
 /* Free the plan's scratch. Safe on NULL. Work already enqueued must be done. */
 void vattn_plan_destroy(vattn_plan_t p);

@@ -28,7 +28,7 @@ class _LazyLib:
 
 _LIB = _LazyLib()
 
-__all__ = ["Plan", "padding_mask", "cross_padding_masks", "describe_plan", "VattnError", "DECODE_AUTO",
+__all__ = ["Plan", "execute_noalloc", "padding_mask", "cross_padding_masks", "describe_plan", "VattnError", "DECODE_AUTO",
            "DECODE_WAVE", "DECODE_MFMA", "ERRBIT_Q_LEN", "ERRBIT_KV_LEN", "ERRBIT_ROWS",
            "ERRBIT_INDEX"]
 
@@ -247,6 +247,35 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def execute_noalloc(B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal, q, k, v, cu_seqlens_q,
+                    cu_seqlens_kv, out, lse, B, err_word=None, stream=None):
+    """One attention pass with no allocation (vattn_execute_noalloc): the plan
+    is chosen per call and its scratch is a static device array shared by
+    every call on the GPU. out / lse / err_word (one int32, or None) are
+    caller-owned device tensors; inputs are packed and contiguous."""
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("out", out, torch.bfloat16),
+                        ("lse", lse, torch.float32), ("cu_seqlens_q", cu_seqlens_q, torch.int32),
+                        ("cu_seqlens_kv", cu_seqlens_kv, torch.int32)):
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    if q.shape[1:] != (Hq, D) or k.shape[1:] != (Hkv, D) or v.shape != k.shape:
+        raise ValueError("q must be [T_q, Hq, D] and k, v [T_kv, Hkv, D]")
+    if out.shape != q.shape or lse.shape != q.shape[:2]:
+        raise ValueError("out must match q and lse must be [T_q, Hq]")
+    if cu_seqlens_q.numel() < B + 1 or cu_seqlens_kv.numel() < B + 1:
+        raise ValueError("cu_seqlens buffers need at least B + 1 entries")
+    if err_word is not None and (err_word.dtype != torch.int32 or not err_word.is_cuda):
+        raise ValueError("err_word must be an int32 device tensor")
+    _lib.check(_LIB.vattn_execute_noalloc(
+        B_max, s_max_q, s_max_kv, Hq, Hkv, D, int(causal), B, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), _ptr(out), _ptr(lse), q.shape[0], k.shape[0],
+        _ptr(err_word) if err_word is not None else None, _stream_of(q, stream)),
+        "vattn_execute_noalloc")
+    return out, lse
 
 
 def cross_padding_masks(cu_seqlens_q, cu_seqlens_kv, B, max_seqlen_q, max_seqlen_kv,

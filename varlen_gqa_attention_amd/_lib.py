@@ -16,6 +16,7 @@ VATTN_ERR_INVALID_ARG = -1
 VATTN_ERR_UNSUPPORTED = -2
 VATTN_ERR_HIP = -3
 VATTN_ERR_OOM = -4
+VATTN_ERR_TOO_LARGE = -5
 
 DECODE_AUTO, DECODE_WAVE, DECODE_MFMA = 0, 1, 2
 ERRBIT_Q_LEN, ERRBIT_KV_LEN, ERRBIT_ROWS, ERRBIT_INDEX = 0x1, 0x2, 0x4, 0x8
@@ -28,7 +29,7 @@ EXPORTS = (
     "vattn_execute_exact_grid", "vattn_padding_mask", "vattn_cross_padding_mask",
     "vattn_plan_error_word",
     "vattn_plan_read_error", "vattn_plan_clear_error", "vattn_plan_set_kernel_events",
-    "vattn_plan_destroy",
+    "vattn_plan_destroy", "vattn_execute_noalloc",
 )
 
 
@@ -117,6 +118,8 @@ def load():
     L.vattn_plan_set_kernel_events.argtypes = [vp, vp, vp]
     L.vattn_plan_destroy.restype = None
     L.vattn_plan_destroy.argtypes = [vp]
+    L.vattn_execute_noalloc.restype = c_int
+    L.vattn_execute_noalloc.argtypes = [c_int] * 8 + [vp] * 7 + [c_i64, c_i64, vp, vp]
     _lib = L
     return L
 

@@ -72,6 +72,8 @@ const char* vattn_status_string(vattn_status s) {
     case VATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case VATTN_ERR_HIP: return "HIP runtime error";
     case VATTN_ERR_OOM: return "out of device memory";
+    case VATTN_ERR_TOO_LARGE:
+      return "the plan's scratch exceeds the static array of vattn_execute_noalloc";
   }
   return "unknown status";
 }
