@@ -116,7 +116,12 @@ typedef struct {
   int force_nsplit;         /* > 0: use this split count (capped by the tile count) */
   int force_decode_path;    /* VATTN_DECODE_* */
   int n_cu_override;        /* > 0: plan as if the device had this many CUs */
-  int fuse_combine;         /* 1: last split workgroup of a unit merges (no 2nd launch); 0/2: combine kernel */
+  int fuse_combine;         /* where split partials merge: 1 = in the split kernel (the last
+                               split workgroup of a unit merges; no second launch);
+                               2 = a separate combine kernel; 0 = automatic: in the split
+                               kernel when all split workgroups fit on the device at once
+                               and the unit count is a multiple of 8, else the combine
+                               kernel */
   int decode_waves;         /* 4 or 8 waves per decode workgroup; 0 = automatic */
   int prefill_grid;         /* prefill: 0 = grid sized from B_max and s_max_q whose
                                workgroups exit on dead tiles (default); 1 = device-built

@@ -84,7 +84,12 @@ def test_describe_pages_rule_equals_oracle_default(B, S, Hq, Hkv, n_cu):
     want = choose_decode_split(B, S, units, n_cu, info["block_n"])
     for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
         assert info[key] == int(want[key]), key
-    assert info["combine_grid"] == (0 if want["direct"] else B * Hq)
+    # merge: in the split kernel when all split workgroups fit the device at
+    # once and the units are a multiple of 8; else a combine kernel of one
+    # workgroup per (sequence, two query heads) at D = 128
+    fused = not want["direct"] and (B * units) % 8 == 0 and want["grid"] <= n_cu
+    assert info["fused_combine"] == int(fused)
+    assert info["combine_grid"] == (0 if want["direct"] or fused else B * -(-Hq // 2))
     same = V.describe_plan(B, 1, S, Hq, Hkv, 128, 0, n_cu_override=n_cu, split_rule="pages")
     assert same == info
 

@@ -229,18 +229,43 @@ def test_b_zero_is_noop():
     assert bool((out == 3.0).all()) and bool((lse == 3.0).all())
 
 
+@pytest.mark.parametrize("B,lens", [(5, [0, 1, 700, 2049, 4000]),   # 10 units: coherent form
+                                    (4, [0, 1, 2049, 4000])])         # 8 units: XCD-local form
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("nsplit", [2, 7, 32])
-def test_fused_merge_equals_combine_kernel_bitwise(path, nsplit):
+def test_fused_merge_equals_combine_kernel_bitwise(path, nsplit, B, lens):
     """The in-kernel merge (last split workgroup) and the combine kernel use
-    the same arithmetic order: identical bits. Repeated launches of the fused
-    plan must also repeat exactly (its arrival counters reset themselves)."""
-    w = _w("fused vs combine", 5, 16, 2, 128, [0, 1, 700, 2049, 4000], s_max_kv=4096)
+    the same arithmetic order: identical bits. With a unit count that is a
+    multiple of 8 the in-kernel merge reads the partials through the XCD's
+    L2 (plain loads), otherwise with cache-bypassing loads."""
+    w = _w("fused vs combine", B, 16, 2, 128, lens, s_max_kv=4096)
     a = run_decode(w, 31, force_decode_path=path, force_nsplit=nsplit, fuse_combine=2)
     assert a["info"]["fused_combine"] == 0 and a["info"]["combine_grid"] > 0
     b = run_decode(w, 31, force_decode_path=path, force_nsplit=nsplit, fuse_combine=1)
     assert b["info"]["fused_combine"] == 1
     assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+
+
+@pytest.mark.parametrize("which", ["long", "batched"])
+def test_fused_merge_full_size_equals_combine_kernel_bitwise(which):
+    """At the long-decode size (8 units x 32 splits, in-kernel merge by
+    default) and at the continuous-batching size (512 units, forced), the
+    XCD-local in-kernel merge equals the combine kernel bit for bit and
+    matches the oracle; repeated launches repeat exactly."""
+    import varlen_gqa_attention_amd as V
+    w = I.long_decode() if which == "long" else I.batched_decode_step(3)
+    fuse = 0 if which == "long" else 1
+    a = run_decode(w, 41, fuse_combine=2)
+    b = run_decode(w, 41, fuse_combine=fuse)
+    assert b["info"]["fused_combine"] == 1 and a["info"]["fused_combine"] == 0
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+    m = I.materialise(w, 41, "cuda")
+    plan = V.Plan(w["B_max"], 1, w["s_max_kv"], w["Hq"], w["Hkv"], w["D"], False,
+                  fuse_combine=fuse)
+    outs = [plan(m["q"], m["k"], m["v"], m["cu_q"], m["cu_kv"], B=w["B"]) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o.view(torch.int16), b["out"].view(torch.int16))
 
 
 def test_fused_plan_repeats_exactly():

@@ -219,12 +219,16 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     a.c = c;
     a.direct = in.direct;
     a.fused = in.fused_combine;
+    // the split-major grid puts unit u's splits on XCD u % 8 when the unit
+    // count is a multiple of the 8 XCDs (workgroups go round-robin to XCDs)
+    a.fused_local = in.fused_combine && (in.n_units % 8 == 0) ? 1 : 0;
     a.kv_idx = gather.idx;
     a.kv_bound = gather.bound;
     int combine_grid = in.combine_grid;
     if (gather.idx && in.fused_combine) {  // gathered keys merge in the combine kernel
       a.fused = 0;
-      combine_grid = in.B_max * in.Hq;
+      const int heads = in.D == 256 ? 1 : 2;  // query heads per combine workgroup
+      combine_grid = in.B_max * ((in.Hq + heads - 1) / heads);
     }
     e = vattn::launch_decode(a, in.decode_path, in.threads / 64, in.grid, combine_grid,
                              st, p->ev_start, p->ev_stop);

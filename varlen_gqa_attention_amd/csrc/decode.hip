@@ -144,59 +144,75 @@ __device__ __forceinline__ void st_part(float* p, float v) {
 }
 
 // LSE merge of split partials of heads [h0, h0 + nh) of sequence b, written
-// as bf16 out and fp32 LSE; one thread per (head, d), nh * D <= blockDim.x.
-// A partial is (O, m, l, lt): lt sums the weights as they entered the P V
-// product (rounded to bf16 on the MFMA path, equal to l on the wave path);
-// O is normalised by the merged lt, so that the output is a weighted mean of
-// V rows with exactly the weights used, and the LSE is taken from l.
-// Used by the combine kernel and by the fused merge, with the same arithmetic
-// in both. Slots are taken in chunks of 32: lane j of each 32-lane half loads
-// slot s0 + j's (m, l) (a half never spans two heads, since D >= 32), the
-// chunk max and the weighted l sum are half-wave reductions, and the weights
-// reach every lane of the half by readlane for the O sum. The first chunk's
-// loads (slots clamped to the allocated nsplit) are issued before `lens()`
-// runs, so the combine kernel reads cu_seqlens while its partials are in
-// flight; lens() returns {query row, n_live}, or n_live < 0 to write nothing.
-// Slots at or past n_live may hold stale values from another launch and are
-// excluded with selects (never multiplied by a zero weight, which would keep
-// a NaN). Chunks after the first merge online (running max, rescaled sums).
+// as bf16 out and fp32 LSE. A partial is (O, m, l, lt): lt sums the weights
+// as they entered the P V product (rounded to bf16 on the MFMA path, equal to
+// l on the wave path); O is normalised by the merged lt, so that the output
+// is a weighted mean of V rows with exactly the weights used, and the LSE is
+// taken from l. Used by the combine kernel and by the in-kernel merge, with
+// the same arithmetic in both.
+//
+// Each head takes kMergeTph(D) = max(32, D / 4) threads, each of which owns 4
+// consecutive d (threads past D / 4 only help with the slot loads), so a
+// 32-lane half never spans two heads; nh * kMergeTph(D) <= blockDim.x. Slots
+// are taken in chunks of 32: lane j of each 32-lane half loads slot s0 + j's
+// (m, l, lt), the chunk max and the weighted sums are half-wave reductions,
+// and the weights reach every lane of the half by readlane for the O sum
+// (16-byte partial loads). The first chunk's loads (slots clamped to the
+// allocated nsplit) are issued before `lens()` runs, so the combine kernel
+// reads cu_seqlens while its partials are in flight; lens() returns
+// {query row, n_live}, or n_live < 0 to write nothing. Slots at or past
+// n_live may hold stale values from another launch and are excluded with
+// selects (never multiplied by a zero weight, which would keep a NaN). Chunks
+// after the first merge online (running max, rescaled sums).
 struct MergeTarget {
   int qrow, n_live;
 };
 
+template <int D>
+constexpr int kMergeTph = D / 4 > 32 ? D / 4 : 32;
+
+template <bool COHERENT>
+__device__ __forceinline__ f32x4 ld_part4(const float* p) {
+  if constexpr (COHERENT) {
+    return f32x4{ld_part<true>(p), ld_part<true>(p + 1), ld_part<true>(p + 2), ld_part<true>(p + 3)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
 template <int D, bool COHERENT, typename Lens>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h0, int nh, Lens lens) {
-  static_assert(D >= 32, "a 32-lane half must not span two heads");
-  const float* pml = reinterpret_cast<const float*>(a.part_ml);
+  constexpr int TPH = kMergeTph<D>;
   constexpr int CH = 32;
+  const float* pml = reinterpret_cast<const float*>(a.part_ml);
   const int idx = threadIdx.x;
   const int lane = idx & 63, sl = lane & 31;
-  const int h = idx / D, d = idx % D;
+  const int h = idx / TPH, dq = idx % TPH;
+  const bool own_d = dq < D / 4;
+  const int d = own_d ? 4 * dq : 0;
   const int hq = h0 + min(h, nh - 1);
   const int64_t base = (int64_t)(b * a.Hq + hq) * a.nsplit;
-  float ms, ls, lts, po[CH];
+  f32x4 ml, po[CH];
   auto load_chunk = [&](int s0, int n_slots) {
-    const int64_t si = base + min(s0 + sl, n_slots - 1);
-    ms = ld_part<COHERENT>(pml + 4 * si);
-    ls = ld_part<COHERENT>(pml + 4 * si + 1);
-    lts = ld_part<COHERENT>(pml + 4 * si + 2);
+    ml = ld_part4<COHERENT>(pml + 4 * (base + min(s0 + sl, n_slots - 1)));
 #pragma unroll
     for (int j = 0; j < CH; ++j)
-      po[j] = ld_part<COHERENT>(a.part_o + (base + min(s0 + j, n_slots - 1)) * D + d);
+      po[j] = ld_part4<COHERENT>(a.part_o + (base + min(s0 + j, n_slots - 1)) * D + d);
   };
   load_chunk(0, a.nsplit);
   const MergeTarget tg = lens();
   if (tg.n_live < 0 || h >= nh) return;  // uniform per 32-lane half
-  float M = kNegInf, L = 0.f, Lt = 0.f, O = 0.f;
+  float M = kNegInf, L = 0.f, Lt = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < tg.n_live; s0 += CH) {
     if (s0 > 0) load_chunk(s0, tg.n_live);
     const bool live = s0 + sl < tg.n_live;
-    const float Mn = fmaxf(M, group_max<32>(live ? ms : kNegInf));
+    const float Mn = fmaxf(M, group_max<32>(live ? ml[0] : kNegInf));
     const float Ms = (Mn == kNegInf) ? 0.f : Mn;
     const float r = fast_exp2(M - Ms);
-    const float wl = live ? fast_exp2(ms - Ms) : 0.f;
-    L = L * r + group_sum<32>(live ? wl * ls : 0.f);
-    Lt = Lt * r + group_sum<32>(live ? wl * lts : 0.f);
+    const float wl = live ? fast_exp2(ml[0] - Ms) : 0.f;
+    L = L * r + group_sum<32>(live ? wl * ml[1] : 0.f);
+    Lt = Lt * r + group_sum<32>(live ? wl * ml[2] : 0.f);
     O *= r;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -204,12 +220,18 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int b, int h
       const float w1 =
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), 32 + j));
       const float wj = (lane & 32) ? w1 : w0;
-      O += (s0 + j < tg.n_live) ? wj * po[j] : 0.f;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      O += (s0 + j < tg.n_live) ? wj * po[j] : z;
     }
     M = Mn;
   }
-  store_out(a, tg.qrow, hq, d, (Lt > 0.f) ? O / Lt : 0.f);
-  if (d == 0) a.lse[(int64_t)tg.qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+  if (!own_d) return;
+  const float inv = (Lt > 0.f) ? 1.f / Lt : 0.f;
+  u32x2 ov;
+  ov[0] = pack_bf16x2(O[0] * inv, O[1] * inv);
+  ov[1] = pack_bf16x2(O[2] * inv, O[3] * inv);
+  *reinterpret_cast<u32x2*>(a.out + (int64_t)tg.qrow * a.o_rs + (int64_t)hq * D + d) = ov;
+  if (dq == 0) a.lse[(int64_t)tg.qrow * a.Hq + hq] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 // Cross-wave merge of per-wave (m, l, O) states held in LDS, then the
@@ -253,7 +275,7 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
     } else {
       const int64_t pidx = ((int64_t)(u.b * a.Hq + hq) * a.nsplit + u.s);
       float* pml = reinterpret_cast<float*>(a.part_ml);
-      if constexpr (FUSED) {
+      if (FUSED && !a.fused_local) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) st_part<true>(a.part_o + pidx * D + d + i, O[i]);
         if (d == 0) {
@@ -268,11 +290,16 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
     }
   }
   if (!FUSED || a.direct) return;
-  // Fused merge. The partials above were written through to memory; once
-  // every thread's stores have completed (the wait below) the workgroup counts
-  // itself in with a system-scope atomic, and the last live split of the unit
-  // reads all partials with cache-bypassing loads and merges them. No L2
-  // write-back or invalidation is needed, unlike a device-scope fence.
+  // In-kernel merge. Once every thread's partial stores have completed (the
+  // wait below) the workgroup counts itself in with an atomic, and the last
+  // live split of the unit reads all of the unit's partials and merges them.
+  // Two forms. XCD-local (fused_local): the plan made every split of a unit
+  // land on one XCD (workgroups go round-robin to the 8 XCDs and the unit
+  // count is a multiple of 8), so plain stores reach that XCD's L2 and plain
+  // loads from another CU of it, whose L1 holds no copy of lines it has not
+  // read in this launch, see them. Otherwise the partials are written through
+  // to memory and read with cache-bypassing loads. Neither needs an L2
+  // write-back or invalidation, unlike a device-scope fence.
   const int n_live = (Lk + a.chunk_keys - 1) / a.chunk_keys;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -285,9 +312,12 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
   }
   __syncthreads();
   if (!*flag) return;
-  for (int hc = 0; hc < nh; hc += NW * 64 / D)
-    merge_partials<D, true>(a, u.b, h0 + hc, min(NW * 64 / D, nh - hc),
-                            [&] { return MergeTarget{qrow, n_live}; });
+  constexpr int HPP = NW * 64 / kMergeTph<D>;  // heads per pass
+  for (int hc = 0; hc < nh; hc += HPP) {
+    auto lens = [&] { return MergeTarget{qrow, n_live}; };
+    if (a.fused_local) merge_partials<D, false>(a, u.b, h0 + hc, min(HPP, nh - hc), lens);
+    else merge_partials<D, true>(a, u.b, h0 + hc, min(HPP, nh - hc), lens);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -686,11 +716,18 @@ __global__ __launch_bounds__(NW * 64) void decode_wave_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // LSE combine kernel: one workgroup per (sequence, query head)
 // ---------------------------------------------------------------------------
+// One 64-thread workgroup per (sequence, 64 / kMergeTph(D) consecutive query
+// heads): two heads at D <= 128, one at D = 256.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+constexpr int kCombineHeads = 64 / kMergeTph<D>;
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int HPW = kCombineHeads<D>;
+  const int hblocks = (a.Hq + HPW - 1) / HPW;
+  const int h0 = (blockIdx.x % hblocks) * HPW, b = blockIdx.x / hblocks;
   if (b >= a.B) return;
-  merge_partials<D, false>(a, b, h, 1, [&] {
+  merge_partials<D, false>(a, b, h0, min(HPW, a.Hq - h0), [&] {
     const Span sq = read_span(a.cu_q, b, a.s_max_q, a.q_rows, kErrQLen);
     const Span sk = read_span(a.cu_kv, b, a.s_max_kv, a.kv_rows, kErrKvLen);
     return MergeTarget{sq.start, sq.len == 0 ? -1 : (sk.len + a.chunk_keys - 1) / a.chunk_keys};
@@ -739,7 +776,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, int path, int nw, int gri
   else launch_split<D, false, false>(a, path, nw, grid, st, ev0, ev1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.fused) return e;
-  decode_combine_kernel<D><<<combine_grid, D < 64 ? 64 : D, 0, st>>>(a);
+  decode_combine_kernel<D><<<combine_grid, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ struct DecodeArgs {
   float c;          // softmax scale * log2(e)
   int direct;       // 1: normalise and write out/lse; 0: write partials
   int fused;        // with direct == 0: 1 = last split workgroup merges, 0 = combine kernel
+  int fused_local;  // fused merge with every split of a unit on one XCD: plain loads/stores
 };
 
 struct PrefillArgs {

@@ -10,16 +10,20 @@
 // looked up once per device (hipGetSymbolAddress) and only that address is
 // ever handed to kernels. Every call on a GPU shares that GPU's array, so
 // calls that overlap on one GPU (two streams, or two host threads) race on
-// it. Nothing in the array must start at zero: the split kernel writes every
-// partial slot the combine kernel reads in the same call, and the merge
-// counters are used only by the in-kernel merge, which the default plan does
-// not select.
+// it. The split kernel writes every partial slot the merge reads in the same
+// call; the merge counters of the in-kernel merge (which the default plan
+// selects when all split workgroups fit the device at once: at most 256
+// units, 1 KiB of counters) must be zero when a call starts: the array is
+// zero when the code object is loaded, the first call on a device also
+// clears the error word and counters with a kernel (unless its stream is
+// being captured), and every merge resets the counters it used.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <mutex>
 
 #include "../../include/vattn.h"
+#include "launch.hpp"
 #include "plan.hpp"
 #include "plan_state.hpp"
 
@@ -37,9 +41,12 @@ namespace {
 std::mutex g_mu;
 uint8_t* g_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
 
+constexpr int kClearWords = 1024;  // error word + merge counters of any plan that uses them
+
 // Device address of this device's `scratch`, looked up on first use with the
-// device current. Returns null on failure.
-uint8_t* scratch_ptr(int dev) {
+// device current (then, if `st` is not capturing, its first words are
+// cleared on `st`). Returns null on failure.
+uint8_t* scratch_ptr(int dev, hipStream_t st) {
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_ptr[dev]) {
     void* ptr = nullptr;
@@ -47,6 +54,11 @@ uint8_t* scratch_ptr(int dev) {
       (void)hipGetLastError();
       return nullptr;
     }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) return nullptr;
+    if (cs == hipStreamCaptureStatusNone &&
+        vattn::launch_clear_words(static_cast<int32_t*>(ptr), kClearWords, st) != hipSuccess)
+      return nullptr;
     g_ptr[dev] = static_cast<uint8_t*>(ptr);
   }
   return g_ptr[dev];
@@ -72,7 +84,7 @@ extern "C" vattn_status vattn_execute_noalloc(int B_max, int s_max_q, int s_max_
   const uint64_t need = vattn::scratch_layout(p.info, nullptr, nullptr);
   if (need > kScratchBytes) return VATTN_ERR_TOO_LARGE;
   if (err_word && ((uintptr_t)err_word & 3)) return VATTN_ERR_INVALID_ARG;
-  uint8_t* base = scratch_ptr(dev);
+  uint8_t* base = scratch_ptr(dev, (hipStream_t)stream);
   if (!base) return VATTN_ERR_HIP;
   p.device = dev;
   p.info.scratch_bytes = (long long)need;

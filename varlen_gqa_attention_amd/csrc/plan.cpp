@@ -98,11 +98,20 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
     // (D = 256 stays at 4 waves: 8 would exceed the register file.)
     in.threads = (in.grid <= n_cu && D <= 128 && in.decode_path == 1) ? 512 : 256;
     if (o.decode_waves == 4 || (o.decode_waves == 8 && D <= 128)) in.threads = 64 * o.decode_waves;
-    // the merge runs in a separate combine kernel unless the in-kernel merge
-    // is asked for (on this chip the in-kernel merge is slower: it saves a
-    // launch but serialises write-through stores, an atomic and the reads)
-    in.fused_combine = (!in.direct && o.fuse_combine == 1) ? 1 : 0;
-    in.combine_grid = (in.direct || in.fused_combine) ? 0 : B_max * Hq;
+    // Where the merge runs. By default in the split kernel (the last split
+    // workgroup of a unit merges) when every split workgroup is resident at
+    // once (grid <= CUs) and each unit's splits share an XCD (units a
+    // multiple of the 8 XCDs, so the partials stay in that XCD's L2): the
+    // merge then overlaps other units' streaming and saves the second
+    // launch (long decode: 32.6 vs 33.7 us/step). Otherwise a separate
+    // combine kernel (with several rounds of workgroups it measured faster).
+    // Option 1 forces the in-kernel merge, 2 the combine kernel.
+    const bool auto_fuse = in.n_units % 8 == 0 && (int64_t)in.n_units * nsplit <= n_cu;
+    in.fused_combine =
+        (!in.direct && (o.fuse_combine == 1 || (o.fuse_combine == 0 && auto_fuse))) ? 1 : 0;
+    // combine: one 64-thread workgroup per (sequence, two query heads), one
+    // head at D = 256
+    in.combine_grid = (in.direct || in.fused_combine) ? 0 : B_max * cdiv(Hq, D == 256 ? 1 : 2);
     in.scratch_bytes = 256;  // error word, aligned
     if (!in.direct)
       in.scratch_bytes += (int64_t)in.n_units * 4 + 256 +

@@ -22,17 +22,21 @@ int main() {
   // one long sequence, 8 KV heads, 256 CUs: the cap of 32 binds
   CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.is_decode && in.nsplit == 32 && in.grid == 256 && in.chunk_keys == 1024 && !in.direct);
-  CHECK(in.decode_path == VATTN_DECODE_MFMA && in.fused_combine == 0 && in.combine_grid == 64);
+  // 8 units x 32 splits = 256 workgroups fit the device at once: in-kernel merge
+  CHECK(in.decode_path == VATTN_DECODE_MFMA && in.fused_combine == 1 && in.combine_grid == 0);
   CHECK(in.threads == 256);
   {
     vattn_plan_opts fu = {};
-    fu.fuse_combine = 1;  // in-kernel merge: no combine launch
+    fu.fuse_combine = 2;  // forced combine kernel
     CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, &fu, 256, &in) == VATTN_OK);
-    CHECK(in.fused_combine == 1 && in.combine_grid == 0 && in.nsplit == 32);
+    CHECK(in.fused_combine == 0 && in.combine_grid == 32 && in.nsplit == 32);
+    fu.fuse_combine = 1;  // forced in-kernel merge
+    CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, &fu, 256, &in) == VATTN_OK);
+    CHECK(in.fused_combine == 1 && in.combine_grid == 0 && in.nsplit == 4);
   }
   // continuous batching: 512 units, 8 workgroups per CU -> 4 splits; G = 4 on the MFMA path
   CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
-  CHECK(!in.direct && in.nsplit == 4 && in.combine_grid == 64 * 32);
+  CHECK(!in.direct && in.nsplit == 4 && in.combine_grid == 64 * 16);
   CHECK(in.decode_path == VATTN_DECODE_MFMA && in.threads == 256);
   // 2048-key lists, 128 units: the work floor (16 tiles per split) gives 2 splits
   CHECK(vattn::plan_compute(16, 1, 2048, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
@@ -92,7 +96,7 @@ int main() {
     pg.min_chunk_tiles = VATTN_PAGES_MIN_CHUNK;
     // tiny decode (2 units, 2 tiles): two splits and a combine
     CHECK(vattn::plan_compute(2, 1, 128, 4, 1, 64, 0, &pg, 256, &in) == VATTN_OK);
-    CHECK(in.nsplit == 2 && !in.direct && in.chunk_keys == 64 && in.combine_grid == 2 * 4);
+    CHECK(in.nsplit == 2 && !in.direct && in.chunk_keys == 64 && in.combine_grid == 2 * 2);
     // long decode: the cap of 32 binds
     CHECK(vattn::plan_compute(1, 1, 32768, 64, 8, 128, 0, &pg, 256, &in) == VATTN_OK);
     CHECK(in.nsplit == 32 && in.grid == 256 && in.chunk_keys == 1024);
