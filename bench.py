@@ -194,9 +194,11 @@ def long_decode(args):
         for i in range(max(1, args.warmup // gsteps)):
             group.replay()
         torch.cuda.synchronize()
-        total, _ = time_replays(seq, len(seq), 0)
+        total, per_rep = time_replays(seq, len(seq), 0)
+        med_step_ms = sorted(per_rep)[len(per_rep) // 2] / gsteps
     else:
-        total, _ = time_replays([g.replay for g in graphs], args.steps, args.warmup)
+        total, per_rep = time_replays([g.replay for g in graphs], args.steps, args.warmup)
+        med_step_ms = sorted(per_rep)[len(per_rep) // 2]
     # execute-level event pairs (split + merge), eager, same stream
     direct = direct_calls(plan, q, ks, vs, cu_q, cu_kv, out, lse, B)
     _, per = time_replays(direct, args.steps, 5)
@@ -215,6 +217,8 @@ def long_decode(args):
     res = dict(
         metric=METRIC, value=round(kv_bytes / (ms * 1e-3) / 1e9, 1), unit="GB/s",
         ms_per_step=round(ms, 5), us_per_step=round(ms * 1e3, 2),
+        us_per_step_median=round(med_step_ms * 1e3, 2),
+        median_note=f"median over {len(per_rep)} graph replays (event pair around each), per step",
         kv_bytes_per_step=kv_bytes, frac_hbm_peak=round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         config=dict(workload="long decode: B=1, Hq=64, Hkv=8, D=128, Lk=32768, bf16 THD, "
                              f"{ncopy} rotating K/V copies (MALL defeat), graphs of {gsteps} step(s)",
@@ -275,6 +279,28 @@ def shard_decode_measure(args, reps=10):
     return res
 
 
+def cold_step_times(step, reps, flush_bytes=640 * 2**20):
+    """Per-step GPU time (HIP events on the stream) of `step` with the
+    Infinity Cache and L2 emptied of its inputs before each step: a read of
+    a buffer larger than twice the 256 MB Infinity Cache runs between steps,
+    outside the event pair (a read leaves no dirty lines to write back)."""
+    torch = _torch()
+    scrub = torch.ones(flush_bytes // 4, device="cuda")
+    sink = torch.empty((), device="cuda")
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for _ in range(3):
+        step()
+    for a, b in evs:
+        torch.sum(scrub, dim=0, out=sink)
+        a.record(st)
+        step()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def small_configs_measure(reps=200):
     """The two remaining decode configurations, graph-replayed: the tiny
     decode (B=2, Hq=4, Hkv=1, D=64, KV lengths U[1,128] seed (0,0)), which is
@@ -296,14 +322,24 @@ def small_configs_measure(reps=200):
         g = capture(lambda: [f() for _ in range(per_graph)])
         total, _ = time_replays([g.replay], reps // per_graph, 2)
         us = total / (reps // per_graph * per_graph) * 1e3
+        # cold: one step per graph replay, caches emptied of the inputs first
+        g1 = capture(f)
+        cold = cold_step_times(g1.replay, 50)
+        us_cold = sorted(cold)[len(cold) // 2] * 1e3
         kv = int(2 * w["kv_lens"].sum() * w["Hkv"] * w["D"] * 2)
-        res[w["name"]] = dict(us_per_step=round(us, 2), kv_bytes=kv,
-                              kv_gbs=round(kv / (us * 1e-6) / 1e9, 1),
+        res[w["name"]] = dict(us_per_step_cold=round(us_cold, 2),
+                              kv_gbs_cold=round(kv / (us_cold * 1e-6) / 1e9, 1),
+                              us_per_step_warm=round(us, 2),
+                              kv_gbs_warm=round(kv / (us * 1e-6) / 1e9, 1), kv_bytes=kv,
                               nsplit=plan.info["nsplit"], grid=plan.info["grid"],
+                              fused_combine=plan.info["fused_combine"],
                               decode_path=("mfma" if plan.info["decode_path"] == 2 else "wave"))
         plan.close()
-    res["note"] = ("graphs of 10 steps on resident K/V (the edge sweep's K/V fit in the 256 MB "
-                   "Infinity Cache at D = 32 and 64, so those rates are cache-assisted)")
+    res["note"] = ("cold: median of 50 single-step graph replays, each after a 640 MiB read "
+                   "that empties the Infinity Cache and L2 of the step's inputs (HIP events "
+                   "around the step only); warm: graphs of 10 back-to-back steps on resident "
+                   "K/V (the edge sweep's K/V fit in the 256 MB Infinity Cache at D = 32 and "
+                   "64, so those warm rates are cache-assisted)")
     return res
 
 
@@ -369,6 +405,54 @@ def cpu_baseline_prefill(budget_s):
         out[name] = dict(value=round(flop / dt / 1e9, 2), unit="GFLOP/s",
                          sample=f"{n} call(s) on one query head of a {L}-token causal sequence "
                                 f"({dt:.2f} s each)")
+    return out
+
+
+def cpu_baseline_configs(prefill_rate_gflops=None):
+    """The oracle timed on each remaining configuration (seconds per step on
+    the host, bounded samples): the tiny decode (whole step, repeated for
+    about a second), the edge sweep at D = 32, 64 and 256 (one whole step
+    each), the continuous-batching decode (steps 0 and 1 of its 100; the
+    lengths differ per step), and the causal varlen prefill extrapolated from
+    the one-head sample's GFLOP/s to the workload's algorithmic flops. Values
+    are drawn on the host (the timing does not depend on them)."""
+    import numpy as np
+    from oracle import attention as A
+    from varlen_gqa_attention_amd import inputs as I
+    out = {}
+
+    def time_step(w, seed, min_s=0.0):
+        m = I.materialise(w, seed, "cpu")
+        q, k, v = (I.bf16_to_f64(m[n]) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            A.attend_varlen(q, k, v, m["cu_q_np"], m["cu_kv_np"], w["B"], w["causal"])
+            n += 1
+            if time.perf_counter() - t0 >= min_s:
+                break
+        return (time.perf_counter() - t0) / n, n
+
+    dt, n = time_step(I.tiny_decode(0), 0, min_s=1.0)
+    out["tiny decode"] = dict(s_per_step=round(dt, 5), sample=f"{n} whole steps")
+    for D in (32, 64, 256):
+        w = I.edge_sweep(D)
+        dt, n = time_step(w, D)
+        out[w["name"]] = dict(s_per_step=round(dt, 3), sample="one whole step")
+    ts = []
+    for t in (0, 1):
+        dt, _ = time_step(I.batched_decode_step(t), t)
+        ts.append(dt)
+    out["continuous-batching decode"] = dict(
+        s_per_step=round(sum(ts) / len(ts), 3),
+        sample="steps 0 and 1 of the 100 (lengths U[128, 8192] each), mean")
+    if prefill_rate_gflops:
+        w = I.varlen_prefill(0)
+        flop = 4 * w["Hq"] * w["D"] * visible_pairs(w["q_lens"], w["kv_lens"])
+        out["causal varlen prefill"] = dict(
+            s_per_step=round(flop / (prefill_rate_gflops * 1e9), 1),
+            sample="extrapolated: the workload's algorithmic flops at the GFLOP/s the oracle "
+                   "reached on one query head of its longest sequence")
     return out
 
 
@@ -504,7 +588,7 @@ def backward_measure(args, reps=10):
                 timing=f"median of {reps} eager calls (dq kernel + dk/dv kernel), HIP events")
 
 
-def batched_decode_measure(args, steps=100):
+def batched_decode_measure(args, steps=100, split_rule=None):
     torch = _torch()
     import numpy as np
     import varlen_gqa_attention_amd as V
@@ -512,7 +596,11 @@ def batched_decode_measure(args, steps=100):
     ws = [I.batched_decode_step(t) for t in range(steps)]
     w = ws[0]
     B, Hq, Hkv, D, smax = w["B"], w["Hq"], w["Hkv"], w["D"], w["s_max_kv"]
-    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False, **args.plan_opts)
+    opts = dict(args.plan_opts)
+    if split_rule is not None:
+        opts.pop("target_blocks_per_cu", None)
+        opts["split_rule"] = split_rule
+    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False, **opts)
     pool = B * smax  # room for B sequences of s_max rows: 1 GiB per K/V tensor
     q = I.normal_bf16((B, Hq, D), 20, "cuda")
     k = I.normal_bf16((pool, Hkv, D), 21, "cuda")
@@ -550,14 +638,28 @@ def batched_decode_measure(args, steps=100):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     assert int(step.item()) == steps
+    # per-step events over a second pass of the same 100 steps, for the median
+    step.zero_()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(st)
+        g.replay()
+        b.record(st)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
     mean_bytes = sum(kv_bytes) / steps
+    info = plan.info
     return dict(workload="continuous-batching decode: B=64, Hq=32, Hkv=8, D=128, s_max_kv=8192, "
                          "lengths U[128,8192] per step (seed 2,t), 100 graph replays",
+                split_rule=split_rule or "default",
                 us_per_step=round(ms * 1e3, 1), kv_gbs=round(mean_bytes / (ms * 1e-3) / 1e9, 1),
+                us_per_step_median=round(per[len(per) // 2] * 1e3, 1),
                 frac_hbm_peak=round(mean_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 host_enqueue_us_per_step=round((t_host1 - t_host0) / steps * 1e6, 1),
-                decode_path=("mfma" if plan.info["decode_path"] == 2 else "wave"),
-                nsplit=plan.info["nsplit"])
+                decode_path=("mfma" if info["decode_path"] == 2 else "wave"),
+                nsplit=info["nsplit"], direct=info["direct"], fused_combine=info["fused_combine"],
+                grid=info["grid"])
 
 
 def mask_measure():
@@ -645,6 +747,8 @@ def main():
     ap.add_argument("--prefill-len", type=int, default=0,
                     help="with --workload prefill: give every sequence this length")
     ap.add_argument("--decode-waves", type=int, default=0, choices=[0, 4, 8])
+    ap.add_argument("--split-rule", default=None, choices=["default", "pages"],
+                    help="with --workload batched_decode: the decode split rule")
     ap.add_argument("--graph-steps", type=int, default=0,
                     help="long decode: steps per captured graph (0 = one per K/V copy)")
     ap.add_argument("--workload", default="long_decode",
@@ -675,7 +779,8 @@ def main():
         fn = {"prefill": prefill_measure, "backward": backward_measure,
               "shard_decode": shard_decode_measure,
               "small_configs": lambda _args: small_configs_measure()}.get(
-                  args.workload, batched_decode_measure)
+                  args.workload,
+                  lambda a: batched_decode_measure(a, split_rule=a.split_rule))
         print(json.dumps({"workload": args.workload, **fn(args)}))
         return
     res, state = long_decode(args)
@@ -687,6 +792,7 @@ def main():
     if not args.no_secondary:
         line["prefill"] = prefill_measure(args)
         line["batched_decode"] = batched_decode_measure(args)
+        line["batched_decode_pages_rule"] = batched_decode_measure(args, split_rule="pages")
         line["gathered_decode"] = gathered_measure()
         line["backward"] = backward_measure(args)
         line["shard_decode"] = shard_decode_measure(args)
@@ -695,7 +801,9 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_long_decode(state, args.cpu_budget)
         if not args.no_secondary:
-            line["cpu_baseline"]["secondary"] = cpu_baseline_prefill(min(5.0, args.cpu_budget))
+            sec = cpu_baseline_prefill(min(5.0, args.cpu_budget))
+            line["cpu_baseline"]["secondary"] = sec
+            line["cpu_baseline"]["per_config"] = cpu_baseline_configs(sec["prefill"]["value"])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line))
