@@ -328,8 +328,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;     // 32-wide k-steps of Q K^T
   constexpr int DB = D / 16;     // 16-wide d blocks of P V
   constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int TILE = 32;       // keys per wave iteration
-  constexpr int DV = D / 16;     // 16-byte V loads per lane per tile
+  // keys per wave iteration: 32 (P V on 16x16x32 MFMAs); 16 at D = 256 (P V on
+  // 16x16x16 MFMAs), so that two tiles in flight fit the registers
+  constexpr int TILE = D == 256 ? 16 : 32;
+  constexpr int KB = TILE / 16;  // 16-key blocks of Q K^T per tile
+  constexpr int DV = TILE * D / 512;  // 16-byte V loads per lane per tile
   constexpr int HPB = 16;        // heads per workgroup
   constexpr int STAGE_BYTES = NW * TILE * D * 2;
   constexpr int MERGE_BYTES = NW * HPB * D * 4 + 4 * NW * HPB * 4;
@@ -399,14 +402,14 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   // tile it loads next (fetched when it issues its current tile, 2 NW tiles
   // ahead), so no K/V load waits on an index load issued after other tiles.
   struct TileRegs {
-    u32x4 k[2][KS], v[DV];
-    int rk[GATHER ? 2 : 1], rv[GATHER ? DV : 1];
+    u32x4 k[KB][KS], v[DV];
+    int rk[GATHER ? KB : 1], rv[GATHER ? DV : 1];
   } A, B;
   auto fetch_rows = [&](int t, TileRegs& r) {
     if constexpr (GATHER) {
       const int key0 = kbeg + t * TILE;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < KB; ++kb2)
         r.rk[kb2] = a.kv_idx[sk.start + min(key0 + 16 * kb2 + hl, kend - 1)];
 #pragma unroll
       for (int i = 0; i < DV; ++i)
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   auto load_tile = [&](int t, TileRegs& r) {
     const int key0 = kbeg + t * TILE;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < KB; ++kb2) {
       const int64_t row = row_of(GATHER ? r.rk[kb2] : min(key0 + 16 * kb2 + hl, kend - 1));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) r.k[kb2][ks] = ld16(kbase + row * krs + 32 * ks + 8 * g4);
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     fetch_rows(t + 2 * NW, r);
   };
 
-  auto process_tile = [&](int t, const u32x4 (&kr)[2][KS], const u32x4 (&vr)[DV]) {
+  auto process_tile = [&](int t, const u32x4 (&kr)[KB][KS], const u32x4 (&vr)[DV]) {
     const int key0 = kbeg + t * TILE;
     // stage V (row-major [key][d], swizzled) in this wave's LDS slice
 #pragma unroll
@@ -440,9 +443,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<u32x4*>(vst + row * D * 2 + swz_tr16<D>(row, c) * 16) = vr[i];
     }
     // S^T = K Q^T for keys [16 kb2, 16 kb2 + 16)
-    f32x4 sacc[2];
+    f32x4 sacc[KB];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+    for (int kb2 = 0; kb2 < KB; ++kb2) {
       sacc[kb2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -450,10 +453,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             __builtin_bit_cast(bf16x8, kr[kb2][ks]), qv[ks], sacc[kb2], 0, 0, 0);
     }
     // online softmax; lane holds keys 16 kb2 + 4 g4 + i of head hl
-    float sc[8];
+    float sc[4 * KB];
     float mx = kNegInf;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = key0 + 16 * kb2 + 4 * g4 + i;
@@ -466,9 +469,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const float msub = (mnew == kNegInf) ? 0.f : mnew;
     const float alpha = fast_exp2(m - msub);
     float psum = 0.f;
-    float p[8];
+    float p[4 * KB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4 * KB; ++i) {
       p[i] = fast_exp2(sc[i] - msub);
       psum += p[i];
     }
@@ -476,30 +479,36 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     m = mnew;
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] *= alpha;
-    u32x4 pw;
-    pw[0] = pack_bf16x2(p[0], p[1]);
-    pw[1] = pack_bf16x2(p[2], p[3]);
-    pw[2] = pack_bf16x2(p[4], p[5]);
-    pw[3] = pack_bf16x2(p[6], p[7]);
+    uint32_t pw[2 * KB];
+#pragma unroll
+    for (int j = 0; j < 2 * KB; ++j) pw[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
     float ptsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2 * KB; ++j)
       ptsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[j]), as_bf16x2(kBf16One2), ptsum, false);
     lt = lt * alpha + ptsum;
-    const bf16x8 pt = __builtin_bit_cast(bf16x8, pw);
 
     wave_lds_sync();
-    // O^T += V^T P^T; V^T operand lane: d = 16 db + hl, keys 4 g4 + j and
-    // 16 + 4 g4 + j (the key order of the P^T operand above)
+    // O^T += V^T P^T; V^T operand lane: d = 16 db + hl, keys 4 g4 + j (and
+    // 16 + 4 g4 + j for 32-key tiles: the key order of the P^T operand above)
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int col = 16 * db + 4 * (hl & 3);
-      const int r1 = 4 * g4 + (hl >> 2), r2 = r1 + 16;
+      const int r1 = 4 * g4 + (hl >> 2);
       const int ch = col >> 3, half = (col >> 2) & 1;
       const bf16x4 x1 = lds_read_tr(vst + r1 * D * 2 + swz_tr16<D>(r1, ch) * 16 + half * 8);
-      const bf16x4 x2 = lds_read_tr(vst + r2 * D * 2 + swz_tr16<D>(r2, ch) * 16 + half * 8);
-      const bf16x8 vt = __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pt, o[db], 0, 0, 0);
+      if constexpr (KB == 2) {
+        const int r2 = r1 + 16;
+        const bf16x4 x2 = lds_read_tr(vst + r2 * D * 2 + swz_tr16<D>(r2, ch) * 16 + half * 8);
+        const bf16x8 vt = __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pt, o[db], 0, 0, 0);
+      } else {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{pw[0], pw[1]});
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, x1), pt, o[db],
+                                                         0, 0, 0);
+      }
     }
     wave_lds_sync();
   };
