@@ -16,9 +16,8 @@ import pytest
 
 from varlen_gqa_attention_amd import build as B
 
-# Known and measured: the 8-wave gathered-key form of the decode MFMA kernel
-# at D = 128 runs only when 8 waves are forced.
-ALLOWED = re.compile(r"decode_mfma_kernelILi128ELi8ELb0ELb1E")
+# Kernels allowed to use scratch memory (none at present).
+ALLOWED = re.compile(r"^$")
 
 KERNEL_SOURCES = ["decode.hip", "prefill.hip", "mask.hip", "bwd.hip", "noalloc.hip"]
 

@@ -68,7 +68,12 @@ struct UnitCoords {
 // Workgroup i = split (i / n_units) of unit (i % n_units): consecutive
 // workgroups are different units at the same split, so with workgroups
 // dispatched round-robin over the 8 XCDs each XCD streams whole units (for
-// 8 units, one KV head per XCD) rather than a slice of every head.
+// 8 units, one KV head per XCD) rather than a slice of every head. Unit
+// r = (b Hkv + j) head_blocks + hb takes KV head (j + b) mod Hkv of sequence
+// b: over a batch the unit slot j, and with it the XCD, cycles through all
+// KV heads instead of always holding the same one (the heads' rows sit at
+// fixed offsets inside each token's row, so a fixed head per XCD keeps each
+// XCD on the same slice of every row).
 __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
   int bid = blockIdx.x;
   UnitCoords u;
@@ -78,8 +83,8 @@ __device__ __forceinline__ UnitCoords unit_of_block(const DecodeArgs& a) {
   u.unit = bid;
   u.hb = bid % a.head_blocks;
   bid /= a.head_blocks;
-  u.hk = bid % a.Hkv;
   u.b = bid / a.Hkv;
+  u.hk = (bid % a.Hkv + u.b) % a.Hkv;
   return u;
 }
 
@@ -324,13 +329,15 @@ __device__ __forceinline__ void finish_workgroup(const DecodeArgs& a, const Unit
 // MFMA path
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool FUSED, bool GATHER>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, D == 128 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;     // 32-wide k-steps of Q K^T
   constexpr int DB = D / 16;     // 16-wide d blocks of P V
   constexpr int CPR = D / 8;     // 16-byte chunks per row
-  // keys per wave iteration: 32 (P V on 16x16x32 MFMAs); 16 at D = 256 (P V on
-  // 16x16x16 MFMAs), so that two tiles in flight fit the registers
-  constexpr int TILE = D == 256 ? 16 : 32;
+  // keys per wave iteration: 32 (P V on 16x16x32 MFMAs) at D <= 64; 16 (P V on
+  // 16x16x16 MFMAs) at D >= 128, so that two tiles in flight fit the
+  // registers of two waves per SIMD at D = 128 (two workgroups per CU) and of
+  // one at D = 256
+  constexpr int TILE = D >= 128 ? 16 : 32;
   constexpr int KB = TILE / 16;  // 16-key blocks of Q K^T per tile
   constexpr int DV = TILE * D / 512;  // 16-byte V loads per lane per tile
   constexpr int HPB = 16;        // heads per workgroup
