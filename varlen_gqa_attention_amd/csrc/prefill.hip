@@ -340,11 +340,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   }
 }
 
-template <int D>
+// Work distribution of a prefill launch; each form is its own kernel, so
+// that each holds one inlined copy of the tile code.
+enum PrefillGrid { kGridSmax = 0, kGridMap = 1, kGridList = 2 };
+
+template <int D, int GRID>
 __global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NSTAGE * 2 * C::TILE_BYTES];
-  if (a.sched_count) {
+  if constexpr (GRID == kGridList) {
     // persistent: stride over (list entry, KV head) pairs; the list is
     // ordered longest query tiles first, so each round of the stride holds
     // tiles of similar cost
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(PrefillCfg<D>::THREADS, 1) void prefill_kernel(Pref
       prefill_tile<D>(a, lds, entry >> 16, f % a.Hkv, entry & 0xffff);
       __syncthreads();  // the next tile reuses the LDS ring
     }
-  } else if (a.tile_map) {
+  } else if constexpr (GRID == kGridMap) {
     const int e = blockIdx.x / a.Hkv;
     if (e >= a.n_map) return;
     const int entry = a.tile_map[e];
@@ -443,15 +447,23 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(Prefill
 // With a measurement event pair the kernel is launched through
 // hipExtLaunchKernelGGL, which stamps the events with the dispatch's own start
 // and end.
+template <int D, int GRID>
+static hipError_t launch_prefill_g(const PrefillArgs& a, int grid, hipStream_t st, hipEvent_t ev0,
+                                   hipEvent_t ev1) {
+  if (ev0)
+    hipExtLaunchKernelGGL(prefill_kernel<D, GRID>, dim3(grid), dim3(PrefillCfg<D>::THREADS), 0, st,
+                          ev0, ev1, 0, a);
+  else
+    prefill_kernel<D, GRID><<<grid, PrefillCfg<D>::THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_prefill_d(const PrefillArgs& a, int grid, hipStream_t st, hipEvent_t ev0,
                                    hipEvent_t ev1) {
-  if (ev0)
-    hipExtLaunchKernelGGL(prefill_kernel<D>, dim3(grid), dim3(PrefillCfg<D>::THREADS), 0, st, ev0,
-                          ev1, 0, a);
-  else
-    prefill_kernel<D><<<grid, PrefillCfg<D>::THREADS, 0, st>>>(a);
-  return hipGetLastError();
+  if (a.sched_count) return launch_prefill_g<D, kGridList>(a, grid, st, ev0, ev1);
+  if (a.tile_map) return launch_prefill_g<D, kGridMap>(a, grid, st, ev0, ev1);
+  return launch_prefill_g<D, kGridSmax>(a, grid, st, ev0, ev1);
 }
 
 static_assert(PrefillCfg<32>::ROWS == prefill_rows(32) && PrefillCfg<64>::ROWS == prefill_rows(64) &&
