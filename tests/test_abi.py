@@ -54,7 +54,7 @@ def test_describe_equals_oracle_rule(B, S, Hq, Hkv, n_cu):
     _lib()
     info = V.describe_plan(B, 1, S, Hq, Hkv, 128, 0, n_cu_override=n_cu)
     units = Hkv * info["head_blocks"]
-    want = choose_decode_split(B, S, units, n_cu, info["block_n"], target_blocks_per_cu=8,
+    want = choose_decode_split(B, S, units, n_cu, info["block_n"], target_blocks_per_cu=16,
                                min_chunk_tiles=16)
     for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
         assert info[key] == int(want[key]), key
@@ -108,13 +108,13 @@ def test_describe_any_target_and_floor_equals_oracle(T, F, B, S, Hq, Hkv):
 
 
 def test_default_rule_constants():
-    """All-zero options select the documented default (8 per CU, 16 tiles)."""
+    """All-zero options select the documented default (16 per CU, 16 tiles)."""
     import varlen_gqa_attention_amd as V
     _lib()
     for B, S in ((1, 32768), (64, 8192), (16, 2048), (2, 128), (33, 16384)):
         a = V.describe_plan(B, 1, S, 32, 8, 128, 0, n_cu_override=256)
         b = V.describe_plan(B, 1, S, 32, 8, 128, 0, n_cu_override=256,
-                            target_blocks_per_cu=8, min_chunk_tiles=16)
+                            target_blocks_per_cu=16, min_chunk_tiles=16)
         assert a == b
     with pytest.raises(ValueError):
         V.describe_plan(1, 1, 64, 8, 8, 64, 0, n_cu_override=256, split_rule="pages",

@@ -173,9 +173,9 @@ def test_one_gpu_share_of_long_decode_with_forced_splits():
 
 
 def test_batched_decode_full_size():
-    # 512 (sequence, kv head) units at 8 workgroups per CU: 4 splits, MFMA path
+    # 512 (sequence, kv head) units at 16 workgroups per CU: 8 splits, MFMA path
     r = run_decode(I.batched_decode_step(0), 0)
-    assert r["info"]["nsplit"] == 4 and r["info"]["decode_path"] == 2
+    assert r["info"]["nsplit"] == 8 and r["info"]["decode_path"] == 2
 
 
 def test_batched_decode_full_size_direct_wave():

@@ -91,7 +91,7 @@ def test_work_floor_per_split():
 
 # (target workgroups per CU, work floor in tiles): the pages' rule (2, 1),
 # this library's default (8, 16), and others around them
-RULES = [(2, 1), (8, 16), (1, 1), (4, 4), (8, 1), (2, 16), (16, 8)]
+RULES = [(2, 1), (16, 16), (8, 16), (1, 1), (4, 4), (8, 1), (2, 16), (16, 8)]
 
 
 def _brute_force_split(B, S, Hkv, n_cu, bn, T, F, cap=32):

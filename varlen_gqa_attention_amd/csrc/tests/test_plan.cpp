@@ -32,11 +32,11 @@ int main() {
     CHECK(in.fused_combine == 0 && in.combine_grid == 32 && in.nsplit == 32);
     fu.fuse_combine = 1;  // forced in-kernel merge
     CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, &fu, 256, &in) == VATTN_OK);
-    CHECK(in.fused_combine == 1 && in.combine_grid == 0 && in.nsplit == 4);
+    CHECK(in.fused_combine == 1 && in.combine_grid == 0 && in.nsplit == 8);
   }
-  // continuous batching: 512 units, 8 workgroups per CU -> 4 splits; G = 4 on the MFMA path
+  // continuous batching: 512 units, 16 workgroups per CU -> 8 splits; G = 4 on the MFMA path
   CHECK(vattn::plan_compute(64, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
-  CHECK(!in.direct && in.nsplit == 4 && in.combine_grid == 64 * 16);
+  CHECK(!in.direct && in.nsplit == 8 && in.combine_grid == 64 * 16);
   CHECK(in.decode_path == VATTN_DECODE_MFMA && in.threads == 256);
   // 2048-key lists, 128 units: the work floor (16 tiles per split) gives 2 splits
   CHECK(vattn::plan_compute(16, 1, 2048, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
@@ -44,8 +44,8 @@ int main() {
   // tiny decode (128 keys): one split, direct write
   CHECK(vattn::plan_compute(2, 1, 128, 4, 1, 64, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.direct && in.nsplit == 1);
-  // batch * kv heads fills the device (8 workgroups per CU): direct write
-  CHECK(vattn::plan_compute(256, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
+  // batch * kv heads fills the device (16 workgroups per CU): direct write
+  CHECK(vattn::plan_compute(512, 1, 8192, 32, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
   CHECK(in.direct && in.nsplit == 1 && in.combine_grid == 0);
   // small groups take the wave path
   CHECK(vattn::plan_compute(64, 1, 8192, 16, 8, 128, 0, nullptr, 256, &in) == VATTN_OK);
@@ -87,7 +87,7 @@ int main() {
           CHECK((in.nsplit - 1) * in.chunk_keys < tiles * 64 && in.nsplit * in.chunk_keys >= S);
           CHECK(in.grid == in.n_units * in.nsplit);
           CHECK(in.direct == (in.nsplit == 1));
-          if (in.n_units >= 8 * 256) CHECK(in.direct);
+          if (in.n_units >= VATTN_DEFAULT_TARGET * 256) CHECK(in.direct);
         }
   {
     // the pages' rule: about two workgroups per CU, no work floor
