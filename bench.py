@@ -614,11 +614,41 @@ def batched_decode_measure(args, steps=100, split_rule=None):
         cus.append(cu)
         kv_bytes.append(int(wt["kv_lens"].sum()) * Hkv * D * 2 * 2)
     cu_all = torch.from_numpy(np.stack(cus)).cuda()
-    live = torch.zeros(1, B + 1, dtype=torch.int32, device="cuda")
-    step = torch.zeros(1, dtype=torch.int64, device="cuda")
+    cu_rows = [cu_all[t] for t in range(steps)]  # contiguous rows, one per step
     cu_q = torch.arange(B + 1, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(B, Hq, device="cuda")
+    st = torch.cuda.current_stream()
+
+    # the 100 steps back to back in one captured graph, each step reading its
+    # own cu_seqlens row: mean time per step
+    def all_steps():
+        for t in range(steps):
+            plan(q, k, v, cu_q, cu_rows[t], out=out, lse=lse, B=B)
+    g_all = capture(all_steps)
+    g_all.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    g_all.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # one graph per step, events around each replay: the median step
+    gs = [capture(lambda t=t: plan(q, k, v, cu_q, cu_rows[t], out=out, lse=lse, B=B))
+          for t in range(steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for g1, (a, b) in zip(gs, evs):
+        a.record(st)
+        g1.replay()
+        b.record(st)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    # the capture-once form: one graph of {select this step's cu on the device,
+    # execute, advance the step counter} replayed 100 times (includes the
+    # selection and counter kernels)
+    live = torch.zeros(1, B + 1, dtype=torch.int32, device="cuda")
+    step = torch.zeros(1, dtype=torch.int64, device="cuda")
 
     def one():
         torch.index_select(cu_all, 0, step, out=live)
@@ -627,35 +657,28 @@ def batched_decode_measure(args, steps=100, split_rule=None):
     g = capture(one)
     step.zero_()
     torch.cuda.synchronize()
-    st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(st)
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(st)
     t_host0 = time.perf_counter()
     for _ in range(steps):
         g.replay()
     t_host1 = time.perf_counter()
-    e1.record(st)
+    e3.record(st)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms_counter = e2.elapsed_time(e3) / steps
     assert int(step.item()) == steps
-    # per-step events over a second pass of the same 100 steps, for the median
-    step.zero_()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record(st)
-        g.replay()
-        b.record(st)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in evs)
     mean_bytes = sum(kv_bytes) / steps
     info = plan.info
     return dict(workload="continuous-batching decode: B=64, Hq=32, Hkv=8, D=128, s_max_kv=8192, "
-                         "lengths U[128,8192] per step (seed 2,t), 100 graph replays",
+                         "lengths U[128,8192] per step (seed 2,t), 100 steps in one captured graph",
                 split_rule=split_rule or "default",
                 us_per_step=round(ms * 1e3, 1), kv_gbs=round(mean_bytes / (ms * 1e-3) / 1e9, 1),
                 us_per_step_median=round(per[len(per) // 2] * 1e3, 1),
+                median_note="one graph per step, HIP events around each replay",
                 frac_hbm_peak=round(mean_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                us_per_step_device_counter=round(ms_counter * 1e3, 1),
+                device_counter_note="one graph of {index_select of the step's cu row, execute, "
+                                    "step += 1} replayed 100 times",
                 host_enqueue_us_per_step=round((t_host1 - t_host0) / steps * 1e6, 1),
                 decode_path=("mfma" if info["decode_path"] == 2 else "wave"),
                 nsplit=info["nsplit"], direct=info["direct"], fused_combine=info["fused_combine"],
