@@ -131,14 +131,47 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   // its own inverse). Tile jt + 1 is issued at the start of iteration jt,
   // into the stage that tile jt - 1 used.
   constexpr int CH = (BN * CPR + C::THREADS - 1) / C::THREADS;  // chunks per thread (K or V)
+  // A full tile's loads take a tile base that is the same for the whole
+  // workgroup (scalar) plus this thread's byte offsets inside the tile, which
+  // do not change from tile to tile (32-bit: row strides below 2^25
+  // elements); only the last, partial tile, or larger strides, clamp the
+  // rows one by one. The LDS destination of a wave's loads is uniform too.
+  // (Up to D = 128, two chunks per thread; at D = 256, eight, whose offsets
+  // would cost the registers the kernel does not have: computed per tile.)
+  constexpr bool kHoist = CH <= 2;
+  const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64;
+  const bool off32 = kHoist && krs < (1 << 25) && vrs < (1 << 25);
+  uint32_t koff[kHoist ? CH : 1], voff[kHoist ? CH : 1];
+  if constexpr (kHoist) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int q = threadIdx.x + i * C::THREADS;
+      const int r = q / CPR, cp = q % CPR;
+      koff[i] = (uint32_t)(r * krs * 2 + swz_rows<D>(r, cp) * 16);
+      voff[i] = (uint32_t)(r * vrs * 2 + swz_tr32<D>(r, cp) * 16);
+    }
+  }
   auto issue_tile = [&](int jt, uint8_t* dst) {
+    const int key0 = jt * BN;
+    if (kHoist && off32 && key0 + BN <= kend) {
+      const uint8_t* kt = reinterpret_cast<const uint8_t*>(kbase + (int64_t)key0 * krs);
+      const uint8_t* vt = reinterpret_cast<const uint8_t*>(vbase + (int64_t)key0 * vrs);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        if (BN * CPR % C::THREADS != 0 && threadIdx.x + i * C::THREADS >= BN * CPR) break;
+        uint8_t* base = dst + (wave0 + i * C::THREADS) * 16;
+        lds_dma16(kt + koff[kHoist ? i : 0], base);
+        lds_dma16(vt + voff[kHoist ? i : 0], base + C::TILE_BYTES);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int q = threadIdx.x + i * C::THREADS;
       if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;  // whole waves
       const int r = q / CPR, cp = q % CPR;
-      const int64_t key = min(jt * BN + r, kend - 1);
-      uint8_t* base = dst + (q - lane) * 16;
+      const int64_t key = min(key0 + r, kend - 1);
+      uint8_t* base = dst + (wave0 + i * C::THREADS) * 16;
       lds_dma16(kbase + key * krs + 8 * swz_rows<D>(r, cp), base);
       lds_dma16(vbase + key * vrs + 8 * swz_tr32<D>(r, cp), base + C::TILE_BYTES);
     }
