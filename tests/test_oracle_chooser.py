@@ -74,7 +74,8 @@ def test_work_floor_per_split():
     # with at least 16 tiles per split: 2048 keys, 128 units -> 2 splits of 1024
     p = choose_decode_split(16, 2048, 8, 256, 64, target_blocks_per_cu=8, min_chunk_tiles=16)
     assert (p["nsplit"], p["chunk_keys"]) == (2, 1024)
-    # 8192 keys, 512 units at 8 per CU -> 4 splits (the floor allows 8)
+    # 8192 keys, 512 units at 8 per CU -> 4 splits (the floor allows 8; the
+    # library's default of 16 per CU takes all 8)
     p = choose_decode_split(64, 8192, 8, 256, 64, target_blocks_per_cu=8, min_chunk_tiles=16)
     assert (p["nsplit"], p["chunk_keys"]) == (4, 2048)
     # 128 keys: one split, direct write

@@ -86,7 +86,7 @@ def test_noalloc_prefill_and_direct_decode():
 
 def test_noalloc_refuses_plans_beyond_the_static_scratch():
     from varlen_gqa_attention_amd import _lib
-    w = I.edge_sweep(128)     # B_max 64 x Hq 128 x 4 splits of fp32 partials: ~17 MB
+    w = I.edge_sweep(128)     # B_max 64 x Hq 128 x 8 splits of fp32 partials: ~35 MB
     import varlen_gqa_attention_amd as V
     info = V.describe_plan(64, 1, 16384, 128, 8, 128, 0)
     assert info["scratch_bytes"] > 8 << 20
