@@ -142,3 +142,60 @@ def test_continuous_batching_full_size_graph_replay():
         assert_out_close(I.bf16_to_f64(outs[i]), ref_o, f"step {t}")
         assert_lse_close(lses[i].cpu().numpy(), ref_l, f"step {t}")
         print(f"[graph full size] step {t} matches the oracle", flush=True)
+
+
+@pytest.mark.timeout(400)
+def test_continuous_batching_hundred_steps_in_one_graph():
+    """The continuous-batching workload as the benchmark times it: its 100
+    steps (B=64, Hq=32, Hkv=8, D=128, s_max_kv=8192, lengths U[128, 8192]
+    per step) captured back to back in one graph, each step reading its own
+    cu_seqlens row and writing its own output slot; replayed twice. Steps 0,
+    1, 50 and 99 match the oracle and, bit for bit, an eager execute."""
+    import varlen_gqa_attention_amd as V
+    steps, sampled = 100, (0, 1, 50, 99)
+    ws = [I.batched_decode_step(t) for t in range(steps)]
+    B, Hq, Hkv, D, smax = 64, 32, 8, 128, 8192
+    cu_all = torch.from_numpy(np.stack([I.cu_from_lengths(w["kv_lens"]) for w in ws])).cuda()
+    cu_rows = [cu_all[t] for t in range(steps)]
+    pool = B * smax
+    q = I.normal_bf16((B, Hq, D), 130, "cuda")
+    k = I.normal_bf16((pool, Hkv, D), 131, "cuda")
+    v = I.normal_bf16((pool, Hkv, D), 132, "cuda")
+    cu_q = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    outs = torch.zeros(steps, B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    lses = torch.zeros(steps, B, Hq, device="cuda")
+    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False)
+    print(f"[graph 100 steps] plan {plan.info}", flush=True)
+
+    def all_steps():
+        for t in range(steps):
+            plan(q, k, v, cu_q, cu_rows[t], out=outs[t], lse=lses[t], B=B)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        all_steps()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="global"):
+        all_steps()
+    torch.cuda.synchronize()
+    outs.zero_()
+    lses.zero_()
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+    print("[graph 100 steps] replays done", flush=True)
+    rows = int(cu_all[list(sampled)].max().item())
+    qf, kf, vf = I.bf16_to_f64(q), I.bf16_to_f64(k[:rows]), I.bf16_to_f64(v[:rows])
+    for t in sampled:
+        o_e, l_e = plan(q, k, v, cu_q, cu_rows[t], B=B)
+        torch.cuda.synchronize()
+        assert torch.equal(o_e.view(torch.int16), outs[t].view(torch.int16)), f"step {t}"
+        assert torch.equal(l_e, lses[t]), f"step {t}"
+        ref_o, ref_l, _ = A.attend_varlen(qf, kf, vf, np.arange(B + 1), cu_rows[t].cpu().numpy(), B,
+                                          False)
+        assert_out_close(I.bf16_to_f64(outs[t]), ref_o, f"step {t}")
+        assert_lse_close(lses[t].cpu().numpy(), ref_l, f"step {t}")
+        print(f"[graph 100 steps] step {t} matches the oracle", flush=True)
