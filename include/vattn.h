@@ -102,16 +102,19 @@ typedef struct vattn_plan_s* vattn_plan_t;
  *     by the tile count and by 32, and write directly once the batch's KV
  *     heads alone fill the device): target_blocks_per_cu = 2,
  *     min_chunk_tiles = 1 (VATTN_PAGES_TARGET, VATTN_PAGES_MIN_CHUNK).
- *   - The default (all fields 0): target_blocks_per_cu = 16,
- *     min_chunk_tiles = 16 (measured faster on this chip: finer splits even
- *     out batches of unequal lengths, and a split keeps at least 1024 keys).
+ *   - The default (all fields 0): target_blocks_per_cu =
+ *     VATTN_DEFAULT_TARGET * 128 / D (16 at D = 128; 64, 32 and 8 at D = 32,
+ *     64 and 256, so that a split workgroup streams about the same bytes at
+ *     every head dimension), min_chunk_tiles = 16 (measured faster on this
+ *     chip: finer splits even out batches of unequal lengths, and a split
+ *     keeps at least 1024 keys).
  */
 #define VATTN_DEFAULT_TARGET 16
 #define VATTN_DEFAULT_MIN_CHUNK 16
 #define VATTN_PAGES_TARGET 2
 #define VATTN_PAGES_MIN_CHUNK 1
 typedef struct {
-  int target_blocks_per_cu; /* 0 = VATTN_DEFAULT_TARGET (16); the pages' rule: 2 */
+  int target_blocks_per_cu; /* 0 = VATTN_DEFAULT_TARGET * 128 / D; the pages' rule: 2 */
   int nsplit_cap;           /* default 32 */
   int force_nsplit;         /* > 0: use this split count (capped by the tile count) */
   int force_decode_path;    /* VATTN_DECODE_* */

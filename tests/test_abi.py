@@ -58,6 +58,13 @@ def test_describe_equals_oracle_rule(B, S, Hq, Hkv, n_cu):
                                min_chunk_tiles=16)
     for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
         assert info[key] == int(want[key]), key
+    # the default target scales with 128 / D (64, 32, 16, 8 workgroups per CU)
+    for D in (32, 64, 256):
+        info = V.describe_plan(B, 1, S, Hq, Hkv, D, 0, n_cu_override=n_cu)
+        want = choose_decode_split(B, S, Hkv * info["head_blocks"], n_cu, info["block_n"],
+                                   target_blocks_per_cu=16 * 128 // D, min_chunk_tiles=16)
+        for key in ("nsplit", "chunk_keys", "grid", "direct", "n_tiles"):
+            assert info[key] == int(want[key]), (D, key)
     # the default s_max grid follows the oracle's grid rule; the scheduled
     # option (prefill_grid=1) is one workgroup per CU over a device-built list
     p = V.describe_plan(B, max(2, S), S, Hq, Hkv, 128, 1, n_cu_override=n_cu)
@@ -108,14 +115,16 @@ def test_describe_any_target_and_floor_equals_oracle(T, F, B, S, Hq, Hkv):
 
 
 def test_default_rule_constants():
-    """All-zero options select the documented default (16 per CU, 16 tiles)."""
+    """All-zero options select the documented default (16 per CU at D = 128,
+    scaled by 128 / D; 16 tiles)."""
     import varlen_gqa_attention_amd as V
     _lib()
     for B, S in ((1, 32768), (64, 8192), (16, 2048), (2, 128), (33, 16384)):
-        a = V.describe_plan(B, 1, S, 32, 8, 128, 0, n_cu_override=256)
-        b = V.describe_plan(B, 1, S, 32, 8, 128, 0, n_cu_override=256,
-                            target_blocks_per_cu=16, min_chunk_tiles=16)
-        assert a == b
+        for D in (32, 64, 128, 256):
+            a = V.describe_plan(B, 1, S, 32, 8, D, 0, n_cu_override=256)
+            b = V.describe_plan(B, 1, S, 32, 8, D, 0, n_cu_override=256,
+                                target_blocks_per_cu=16 * 128 // D, min_chunk_tiles=16)
+            assert a == b
     with pytest.raises(ValueError):
         V.describe_plan(1, 1, 64, 8, 8, 64, 0, n_cu_override=256, split_rule="pages",
                         target_blocks_per_cu=2)

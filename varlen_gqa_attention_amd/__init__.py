@@ -35,7 +35,8 @@ __all__ = ["Plan", "execute_noalloc", "padding_mask", "cross_padding_masks", "de
 
 # Decode split rules (include/vattn.h, vattn_plan_opts): "pages" is the rule
 # the split-K pages state (about two workgroups per CU, no work floor);
-# "default" is this library's tuned default (16 per CU, 16 tiles per split).
+# "default" is this library's tuned default (16 per CU at D = 128, scaled by
+# 128 / D; 16 tiles per split).
 SPLIT_RULES = {"default": dict(target_blocks_per_cu=0, min_chunk_tiles=0),
                "pages": dict(target_blocks_per_cu=2, min_chunk_tiles=1)}
 

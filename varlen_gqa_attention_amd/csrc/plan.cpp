@@ -15,11 +15,13 @@
 // "tile count" is ceil(s_max_kv / 64); splits are contiguous chunks of whole
 // tiles and the count is recomputed from the chunk size so that no split is
 // empty at s_max_kv. The pages' rule is a plan option (target 2 workgroups
-// per CU, no work floor). The default is tuned for this chip: 8 workgroups
-// per CU measured best (a CU holds several decode workgroups at once, and
-// finer splits even out batches whose lengths vary, where the longest
-// sequence's workgroup would otherwise set the step time); the rule's form,
-// caps and direct-write fallback are unchanged. One bound is added by
+// per CU, no work floor). The default is tuned for this chip: 16 workgroups
+// per CU at D = 128, scaled by 128 / D (a CU holds several decode
+// workgroups at once, each of which streams at a rate set by the bytes it
+// keeps in flight, and finer splits even out batches whose lengths vary,
+// where the longest sequence's workgroup would otherwise set the step time;
+// at larger D a split's bytes grow, at smaller D they shrink); the rule's
+// form, caps and direct-write fallback are unchanged. One bound is added by
 // default: a split keeps at least 16 tiles (1024 keys) at s_max_kv, below
 // which the per-workgroup start and merge cost more than the parallelism
 // returns (measured on 2048-key gathered lists and 8192-key batches).
@@ -42,7 +44,8 @@ vattn_status plan_compute(int B_max, int s_max_q, int s_max_kv, int Hq, int Hkv,
   if (D != 32 && D != 64 && D != 128 && D != 256) return VATTN_ERR_UNSUPPORTED;
   vattn_plan_opts o = {};
   if (opts) o = *opts;
-  const int target = o.target_blocks_per_cu > 0 ? o.target_blocks_per_cu : kDecodeTargetPerCu;
+  const int target =
+      o.target_blocks_per_cu > 0 ? o.target_blocks_per_cu : kDecodeTargetPerCu * 128 / D;
   const int cap = o.nsplit_cap > 0 ? o.nsplit_cap : 32;
   const int min_chunk = o.min_chunk_tiles > 0 ? o.min_chunk_tiles : kMinChunkTiles;
   const int G = Hq / Hkv;

@@ -11,7 +11,8 @@ constexpr int kDecodeMfmaHeads = 16;  // heads per workgroup on the MFMA decode 
 constexpr int kDecodeWaveHeads = 4;   // heads per workgroup on the wave decode path
 constexpr int kWaveMaxG = 3;          // auto: G <= this uses the wave path (MFMA measured
                                       // faster from G = 4 on)
-constexpr int kDecodeTargetPerCu = VATTN_DEFAULT_TARGET;  // split rule: workgroups per CU to aim for
+// split rule: workgroups per CU to aim for at D = 128 (scaled by 128 / D)
+constexpr int kDecodeTargetPerCu = VATTN_DEFAULT_TARGET;
 constexpr int kMinChunkTiles = VATTN_DEFAULT_MIN_CHUNK;   // split rule: fewest KV tiles per split
 // query rows (heads x tokens) per prefill workgroup: 8 waves (4 for D = 256)
 // of 32 rows; threads per prefill workgroup

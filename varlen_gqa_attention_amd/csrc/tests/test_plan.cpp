@@ -87,7 +87,7 @@ int main() {
           CHECK((in.nsplit - 1) * in.chunk_keys < tiles * 64 && in.nsplit * in.chunk_keys >= S);
           CHECK(in.grid == in.n_units * in.nsplit);
           CHECK(in.direct == (in.nsplit == 1));
-          if (in.n_units >= VATTN_DEFAULT_TARGET * 256) CHECK(in.direct);
+          if (in.n_units >= VATTN_DEFAULT_TARGET * 2 * 256) CHECK(in.direct);  // D = 64: 2x target
         }
   {
     // the pages' rule: about two workgroups per CU, no work floor
