@@ -6,8 +6,9 @@
 Default workload: long decode, B=1, Hq=64, Hkv=8 (G=8), D=128, one query
 token over 32768 keys (split-KV: 32 splits x 8 KV heads = 256 workgroups).
 A step is one execute of the plan (split kernel + merge) replayed from a
-captured HIP graph, with inputs resident in HBM. K/V rotate over enough
-copies (> 2x the 256 MB Infinity Cache) that every step reads from HBM.
+captured HIP graph of up to 40 steps, with inputs resident in HBM. K/V rotate
+over enough copies (> 2x the 256 MB Infinity Cache) that every step reads from
+HBM.
 
 Prints ONE JSON line: value = KV GB/s over the K timed steps (whole job, one
 GPU), roofline of the dominant kernel (algorithmic bytes per launch / mean
@@ -184,21 +185,27 @@ def long_decode(args):
         k, v = ks[i], vs[i]
         fns.append(lambda k=k, v=v: plan(q, k, v, cu_q, cu_kv, out=out, lse=lse, B=B))
     graphs = [capture(f) for f in fns]
-    gsteps = args.graph_steps if args.graph_steps > 0 else ncopy
+    # one graph holds gsteps consecutive steps (one per K/V copy, in turn), as
+    # a model's captured decode forward holds one attention call per layer
+    # (up to 40 here); each graph replay adds a fixed ~5 us boundary, which a
+    # short graph would charge to few steps
+    gsteps = args.graph_steps if args.graph_steps > 0 else min(40, max(ncopy, args.steps))
     if gsteps > 1:
-        # one graph holds gsteps consecutive steps (one per K/V copy, in turn),
-        # as a model's captured forward holds one attention call per layer
         group = capture(lambda: [fns[i % ncopy]() for i in range(gsteps)])
         seq = [group.replay] * (args.steps // gsteps) + \
               [graphs[i % ncopy].replay for i in range(args.steps % gsteps)]
         for i in range(max(1, args.warmup // gsteps)):
             group.replay()
         torch.cuda.synchronize()
-        total, per_rep = time_replays(seq, len(seq), 0)
+        total, _ = time_replays(seq, len(seq), 0)
+        # the median step: 50 replays of the graph, event pair around each
+        _, per_rep = time_replays([group.replay], 50, 2)
         med_step_ms = sorted(per_rep)[len(per_rep) // 2] / gsteps
+        n_med = len(per_rep)
     else:
         total, per_rep = time_replays([g.replay for g in graphs], args.steps, args.warmup)
         med_step_ms = sorted(per_rep)[len(per_rep) // 2]
+        n_med = len(per_rep)
     # execute-level event pairs (split + merge), eager, same stream
     direct = direct_calls(plan, q, ks, vs, cu_q, cu_kv, out, lse, B)
     _, per = time_replays(direct, args.steps, 5)
@@ -218,7 +225,8 @@ def long_decode(args):
         metric=METRIC, value=round(kv_bytes / (ms * 1e-3) / 1e9, 1), unit="GB/s",
         ms_per_step=round(ms, 5), us_per_step=round(ms * 1e3, 2),
         us_per_step_median=round(med_step_ms * 1e3, 2),
-        median_note=f"median over {len(per_rep)} graph replays (event pair around each), per step",
+        median_note=f"median over {n_med} replays of the {gsteps}-step graph (event pair around "
+                    "each), per step",
         kv_bytes_per_step=kv_bytes, frac_hbm_peak=round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         config=dict(workload="long decode: B=1, Hq=64, Hkv=8, D=128, Lk=32768, bf16 THD, "
                              f"{ncopy} rotating K/V copies (MALL defeat), graphs of {gsteps} step(s)",
@@ -773,7 +781,7 @@ def main():
     ap.add_argument("--split-rule", default=None, choices=["default", "pages"],
                     help="with --workload batched_decode: the decode split rule")
     ap.add_argument("--graph-steps", type=int, default=0,
-                    help="long decode: steps per captured graph (0 = one per K/V copy)")
+                    help="long decode: steps per captured graph (0 = min(40, --steps))")
     ap.add_argument("--workload", default="long_decode",
                     choices=["long_decode", "prefill", "batched_decode", "gathered_decode",
                              "backward", "shard_decode", "small_configs"],
