@@ -250,8 +250,10 @@ vattn_status vattn_execute_gathered(vattn_plan_t p, int B,
  * and v as slices of one fused QKV buffer). Row t of q starts at element
  * t * q_row_stride of q (likewise k, v and out); within a row the heads are
  * contiguous with stride D. A stride of 0 means packed (H * D). Each stride
- * must be >= H * D of its tensor and a multiple of 8 elements (16 bytes);
- * otherwise VATTN_ERR_INVALID_ARG and nothing is enqueued. q_rows / kv_rows
+ * must be >= H * D of its tensor and a multiple of 8 elements (16 bytes),
+ * and for prefill plans the k and v strides below 2^25 elements (the
+ * prefill kernel addresses a 64-key tile with 32-bit offsets from its first
+ * row); otherwise VATTN_ERR_INVALID_ARG and nothing is enqueued. q_rows / kv_rows
  * count rows: the caller's buffers must hold (rows - 1) * stride + H * D
  * elements. lse stays packed [T_q, Hq]. Same results as vattn_execute on
  * packed copies (bit-identical).

@@ -85,6 +85,53 @@ def test_prefill_on_fused_qkv_slices(grid, D):
     _check(plan, lens, lens, Hq, Hkv, D, True, 40 + D)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_prefill_with_the_widest_kv_rows(D):
+    """K and V rows 2^25 - 8 elements apart (64 MiB per token row), the widest
+    a prefill plan accepts: the kernel's 32-bit tile offsets reach their
+    largest values. Equal to the packed call bit for bit, and the oracle;
+    rows 2^25 elements apart or more are rejected before anything is
+    enqueued."""
+    import varlen_gqa_attention_amd as V
+    from varlen_gqa_attention_amd import _lib
+    Hq, Hkv = 4, 1
+    lens = [3, 2]
+    cu = I.cu_from_lengths(lens)
+    T = int(cu[-1])
+    stride = (1 << 25) - 8
+    print(f"[wide rows] D={D} stride={stride}", flush=True)
+    plan = V.Plan(len(lens), 8, 8, Hq, Hkv, D, True)
+    q = I.normal_bf16((T, Hq, D), 60 + D, "cuda")
+    kp = I.normal_bf16((T, Hkv, D), 61 + D, "cuda")
+    vp = I.normal_bf16((T, Hkv, D), 62 + D, "cuda")
+    store = torch.zeros(2, (T - 1) * stride + Hkv * D, dtype=torch.bfloat16, device="cuda")
+    k = store[0].as_strided((T, Hkv, D), (stride, D, 1))
+    v = store[1].as_strided((T, Hkv, D), (stride, D, 1))
+    k.copy_(kp)
+    v.copy_(vp)
+    c = torch.from_numpy(cu).cuda()
+    out_p, lse_p = plan(q, kp, vp, c, c, B=len(lens))
+    out_w, lse_w = plan(q, k, v, c, c, B=len(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(out_p.view(torch.int16), out_w.view(torch.int16))
+    assert torch.equal(lse_p, lse_w)
+    ro, rl, wr = A.attend_varlen(I.bf16_to_f64(q), I.bf16_to_f64(kp), I.bf16_to_f64(vp), cu, cu,
+                                 len(lens), True)
+    assert_out_close(I.bf16_to_f64(out_w)[wr], ro[wr])
+    assert_lse_close(lse_w.cpu().numpy()[wr], rl[wr])
+    # one row 2^25 elements apart: rejected, out untouched
+    L = _lib.load()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    out_r = torch.full_like(out_p, 7.0)
+    for ks, vs in ((1 << 25, 0), (0, 1 << 25), ((1 << 25) + 8, (1 << 25) + 8)):
+        st = L.vattn_execute_strided(plan._h, len(lens), P(q), 0, P(store[0]), ks, P(store[1]),
+                                     vs, P(c), P(c), P(out_r), 0, P(lse_w), T, 2, None)
+        assert st == -1, (ks, vs, st)
+    torch.cuda.synchronize()
+    assert bool((out_r == 7.0).all())
+    del store
+
+
 def test_invalid_strides_are_rejected():
     import varlen_gqa_attention_amd as V
     from varlen_gqa_attention_amd import _lib

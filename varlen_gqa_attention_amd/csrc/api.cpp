@@ -233,6 +233,9 @@ static vattn_status run(vattn_plan_t p, int B, const void* q, const void* k, con
     e = vattn::launch_decode(a, in.decode_path, in.threads / 64, in.grid, combine_grid,
                              st, p->ev_start, p->ev_stop);
   } else {
+    // the prefill kernel addresses a K or V tile with 32-bit offsets from
+    // its first row: rows below 2^25 elements apart
+    if (rs.k >= (int64_t(1) << 25) || rs.v >= (int64_t(1) << 25)) return VATTN_ERR_INVALID_ARG;
     vattn::PrefillArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;

@@ -49,11 +49,20 @@ __device__ __forceinline__ bf16x4 bwd_read_tr(const uint8_t* p) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// Direct global -> LDS load of 16 bytes per lane through a buffer resource
+// (raw, byte offset voff from the resource's base): lane l's bytes land at
 // lds_base + 16 l (lds_base must be the same for the whole wave). Completion
-// is counted by vmcnt like any vector-memory load.
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+// is counted by vmcnt like any vector-memory load. (With the global-address
+// form in flight the compiler would make every LDS read wait for all earlier
+// ones; with buffer loads it counts them.)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Resource over the bytes from `base` on (no size limit: the kernel forms
+// in-range offsets only), 32-bit data format (gfx9).
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
 }
 
 __device__ __forceinline__ void bwd_wait_vmem() {
@@ -392,16 +401,15 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   bool st_dead = false;
   // Per-step addressing (uniform), then the loads in parts: part i = chunk i
   // of the Q and dO tiles, spread over the step's first MFMA region.
-  const uint16_t* st_qb = a.q;
-  const uint16_t* st_db = a.dout;
+  rsrc_t st_rq = raw_rsrc(a.q), st_rd = raw_rsrc(a.dout);
   int st_rlim = 0;
   auto issue_begin = [&](int it) {
     const int tb = it / a.G, hq = hk * a.G + it % a.G;
     const int tbase = t_first + tb * BN;
     const int rlim = Lq - 1 - tbase;
     const int64_t t0 = (int64_t)sq.start + tbase;
-    st_qb = a.q + t0 * a.q_rs + hq * D;
-    st_db = a.dout + t0 * a.do_rs + hq * D;
+    st_rq = raw_rsrc(a.q + t0 * a.q_rs + hq * D);
+    st_rd = raw_rsrc(a.dout + t0 * a.do_rs + hq * D);
     st_rlim = rlim;
     if (threadIdx.x < BN) {
       const uint32_t rr = (uint32_t)min((int)threadIdx.x, rlim);
@@ -417,8 +425,9 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
     const uint32_t rr = (uint32_t)min(r, st_rlim);
     const uint32_t c8 = 8 * swz_dual<D>(r, q % CPR);
     uint8_t* base = dst + (q - lane) * 16;
-    lds_dma16(st_qb + (__umul24(rr, (uint32_t)a.q_rs) + c8), base);
-    lds_dma16(st_db + (__umul24(rr, (uint32_t)a.do_rs) + c8), base + TILE);
+    // byte offsets below 2^31: rows < 64 apart, row strides < 2^24 elements
+    lds_dma16(st_rq, 2 * (__umul24(rr, (uint32_t)a.q_rs) + c8), base);
+    lds_dma16(st_rd, 2 * (__umul24(rr, (uint32_t)a.do_rs) + c8), base + TILE);
   };
   auto issue_step = [&](int it, uint8_t* dst) {
     issue_begin(it);

@@ -43,11 +43,22 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// Direct global -> LDS load of 16 bytes per lane through a buffer resource
+// (raw, byte offset voff from the resource's base): lane l's bytes land at
 // lds_base + 16 l (lds_base must be the same for the whole wave). Completion
-// is counted by vmcnt like any vector-memory load.
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_base, 16, 0, 0);
+// is counted by vmcnt like any vector-memory load. The buffer form rather
+// than the global-address form: while a global-address load to LDS is in
+// flight the compiler makes every LDS read wait for all earlier ones
+// (lgkmcnt(0)), so the K and V fragment reads of a tile could not run ahead
+// of the MFMAs that consume them; with buffer loads it counts them.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Resource over the bytes from `base` on: no size limit (every offset the
+// kernel forms is in range by construction), 32-bit data format (gfx9).
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(0) with the other counters untouched (gfx9 encoding).
@@ -129,18 +140,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   // swizzle applied on the global side: the lane that fills slot (row r,
   // position c') loads chunk swz(r, c') of the row (each swizzle is an XOR,
   // its own inverse). Tile jt + 1 is issued at the start of iteration jt,
-  // into the stage that tile jt - 1 used.
+  // into the stage that tile jt - 1 used. Rows past the keys are clamped to
+  // the last key (masked later).
   constexpr int CH = (BN * CPR + C::THREADS - 1) / C::THREADS;  // chunks per thread (K or V)
-  // A full tile's loads take a tile base that is the same for the whole
-  // workgroup (scalar) plus this thread's byte offsets inside the tile, which
-  // do not change from tile to tile (32-bit: row strides below 2^25
-  // elements); only the last, partial tile, or larger strides, clamp the
-  // rows one by one. The LDS destination of a wave's loads is uniform too.
-  // (Up to D = 128, two chunks per thread; at D = 256, eight, whose offsets
-  // would cost the registers the kernel does not have: computed per tile.)
-  constexpr bool kHoist = CH <= 2;
   const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64;
-  const bool off32 = kHoist && krs < (1 << 25) && vrs < (1 << 25);
+  // One buffer resource per tile (its first key row) and 32-bit byte offsets
+  // inside it: 63 rows of a stride below 2^25 elements (the host rejects
+  // wider K and V rows) plus one row stay below 2^32 bytes. A full tile's
+  // offsets do not change from tile to tile: computed once (up to D = 128,
+  // two chunks per thread; at D = 256, eight, whose offsets would cost the
+  // registers the kernel does not have: computed per tile).
+  constexpr bool kHoist = CH <= 2;
   uint32_t koff[kHoist ? CH : 1], voff[kHoist ? CH : 1];
   if constexpr (kHoist) {
 #pragma unroll
@@ -153,15 +163,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   }
   auto issue_tile = [&](int jt, uint8_t* dst) {
     const int key0 = jt * BN;
-    if (kHoist && off32 && key0 + BN <= kend) {
-      const uint8_t* kt = reinterpret_cast<const uint8_t*>(kbase + (int64_t)key0 * krs);
-      const uint8_t* vt = reinterpret_cast<const uint8_t*>(vbase + (int64_t)key0 * vrs);
+    const rsrc_t rk = raw_rsrc(kbase + (int64_t)key0 * krs);
+    const rsrc_t rv = raw_rsrc(vbase + (int64_t)key0 * vrs);
+    if (kHoist && key0 + BN <= kend) {
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         if (BN * CPR % C::THREADS != 0 && threadIdx.x + i * C::THREADS >= BN * CPR) break;
         uint8_t* base = dst + (wave0 + i * C::THREADS) * 16;
-        lds_dma16(kt + koff[kHoist ? i : 0], base);
-        lds_dma16(vt + voff[kHoist ? i : 0], base + C::TILE_BYTES);
+        lds_dma16(rk, koff[kHoist ? i : 0], base);
+        lds_dma16(rv, voff[kHoist ? i : 0], base + C::TILE_BYTES);
       }
       return;
     }
@@ -170,10 +180,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
       const int q = threadIdx.x + i * C::THREADS;
       if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;  // whole waves
       const int r = q / CPR, cp = q % CPR;
-      const int64_t key = min(key0 + r, kend - 1);
+      const uint32_t rr = (uint32_t)(min(key0 + r, kend - 1) - key0);
       uint8_t* base = dst + (wave0 + i * C::THREADS) * 16;
-      lds_dma16(kbase + key * krs + 8 * swz_rows<D>(r, cp), base);
-      lds_dma16(vbase + key * vrs + 8 * swz_tr32<D>(r, cp), base + C::TILE_BYTES);
+      lds_dma16(rk, rr * (uint32_t)(krs * 2) + 16 * swz_rows<D>(r, cp), base);
+      lds_dma16(rv, rr * (uint32_t)(vrs * 2) + 16 * swz_tr32<D>(r, cp), base + C::TILE_BYTES);
     }
   };
 
