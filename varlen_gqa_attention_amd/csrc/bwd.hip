@@ -389,6 +389,12 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   const int t_first = a.causal ? max(0, j0 - shift) : 0;
   const int n_tb = Lq > t_first ? (Lq - t_first + BN - 1) / BN : 0;
   const int n_it = n_tb * a.G;
+  // Step it covers row block tb_of(it), last block first: the key tiles of a
+  // sequence start at different rows (causal) but all end at its last one,
+  // so walking down from there keeps the workgroups of a sequence and KV
+  // head (one XCD) on the same Q and dO rows at the same time, which then
+  // come from that XCD's L2.
+  auto tb_of = [&](int it) { return n_tb - 1 - it / a.G; };
 
   // Staging: the Q and dO tiles of a step go straight from global memory to
   // LDS (lds_dma16); the lane that fills slot (row r, position c') of the
@@ -404,7 +410,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
   rsrc_t st_rq = raw_rsrc(a.q), st_rd = raw_rsrc(a.dout);
   int st_rlim = 0;
   auto issue_begin = [&](int it) {
-    const int tb = it / a.G, hq = hk * a.G + it % a.G;
+    const int tb = tb_of(it), hq = hk * a.G + it % a.G;
     const int tbase = t_first + tb * BN;
     const int rlim = Lq - 1 - tbase;
     const int64_t t0 = (int64_t)sq.start + tbase;
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(BwdCfg<D>::THREADS, 1) void bwd_dkdv_kernel(BwdArgs
     if (more) issue_begin(it + 1);
     const uint8_t* ldo = lq + TILE;
     const float* lrow = reinterpret_cast<const float*>(lq + 2 * TILE);
-    const int tbase = t_first + (it / a.G) * BN;
+    const int tbase = t_first + tb_of(it) * BN;
     // Per step, two 32-row halves in a software pipeline, so that each
     // half's softmax-gradient VALU work runs under the other half's MFMAs:
     //   A: S, dP of rows 0-31
