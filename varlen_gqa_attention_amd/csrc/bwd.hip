@@ -31,9 +31,8 @@
 //    4 waves and the dk/dv kernel steps over 32 rows, to fit the registers.
 // Every contraction is v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and
 // dS are rounded to bf16 as MFMA operands. Tiles pass through a two-stage
-// LDS ring with one barrier per step: the dq kernel's K/V tiles through
-// registers (loads two steps ahead), the dk/dv kernel's Q/dO tiles by
-// direct-to-LDS loads (one step ahead; measured equal in the dq kernel).
+// LDS ring with one barrier per step, filled by direct-to-LDS loads one
+// step ahead (the dq kernel's K/V tiles, the dk/dv kernel's Q/dO tiles).
 #include <hip/hip_ext.h>
 
 #include "device.hpp"
@@ -203,31 +202,32 @@ __global__ __launch_bounds__((BwdCfg<D, dq_waves<D>()>::THREADS)) void bwd_dq_ke
   const uint16_t* kbase = a.k + (int64_t)sk.start * krs + hk * D;
   const uint16_t* vbase = a.v + (int64_t)sk.start * vrs + hk * D;
   const int ntiles = (kend + BN - 1) / BN;
-  u32x4 stk[CH], stv[CH];
-  auto load_tile = [&](int jt) {
+  // K and V tiles go straight into a two-stage LDS ring (buffer-resource
+  // loads, one resource per tile at its first key row; byte offsets below
+  // 2^31: rows < 64 apart, row strides < 2^24 elements): the lane that fills
+  // slot (row r, position c') loads chunk swz_dual(r, c') of the row (the
+  // swizzle is an XOR, its own inverse). Rows past the keys are clamped to
+  // the last key (masked later). Tile jt + 1 is issued at the start of
+  // iteration jt, into the stage that tile jt - 1 used.
+  const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 64;
+  auto issue_tile = [&](int jt, uint8_t* dst) {
+    const int key0 = jt * BN;
+    const rsrc_t rk = raw_rsrc(kbase + (int64_t)key0 * krs);
+    const rsrc_t rv = raw_rsrc(vbase + (int64_t)key0 * vrs);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
+      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;  // whole waves
       const int r = q / CPR, c = q % CPR;
-      const int64_t key = min(jt * BN + r, kend - 1);
-      stk[i] = ld16(kbase + key * krs + 8 * c);
-      stv[i] = ld16(vbase + key * vrs + 8 * c);
+      const uint32_t rr = (uint32_t)(min(key0 + r, kend - 1) - key0);
+      const uint32_t c16 = 16 * swz_dual<D>(r, c);
+      uint8_t* base = dst + (wave0 + i * C::THREADS) * 16;
+      lds_dma16(rk, rr * (uint32_t)(krs * 2) + c16, base);
+      lds_dma16(rv, rr * (uint32_t)(vrs * 2) + c16, base + C::TILE_BYTES);
     }
   };
-  auto store_tile = [&](int jt) {
-    uint8_t* sk_ = lds + (jt & 1) * 2 * C::TILE_BYTES;
-    uint8_t* sv_ = sk_ + C::TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = threadIdx.x + i * C::THREADS;
-      if (BN * CPR % C::THREADS != 0 && q >= BN * CPR) break;
-      const int r = q / CPR, c = q % CPR;
-      *reinterpret_cast<u32x4*>(sk_ + r * D * 2 + swz_dual<D>(r, c) * 16) = stk[i];
-      *reinterpret_cast<u32x4*>(sv_ + r * D * 2 + swz_dual<D>(r, c) * 16) = stv[i];
-    }
-  };
-  if (ntiles > 0) load_tile(0);
+  // tile 0's loads share the Q / dO / O loads' round trip
+  if (ntiles > 0) issue_tile(0, lds);
   bwd_wait_vmem();
 
   delta = sum_xor32(delta);
@@ -243,16 +243,11 @@ __global__ __launch_bounds__((BwdCfg<D, dq_waves<D>()>::THREADS)) void bwd_dq_ke
 #pragma unroll
     for (int j = 0; j < 16; ++j) dq[i][j] = 0.f;
 
-  if (ntiles > 0) store_tile(0);
-  if (ntiles > 1) load_tile(1);
-
-  for (int jt = 0; jt < ntiles; ++jt) {
-    __syncthreads();
-    if (jt + 1 < ntiles) {
-      store_tile(jt + 1);
-      if (jt + 2 < ntiles) load_tile(jt + 2);
-    }
-    const uint8_t* lk = lds + (jt & 1) * 2 * C::TILE_BYTES;
+  // One tile: issue tile jt + 1 into the other stage, then compute tile jt.
+  // The stages are disjoint (restrict), which lets the compiler read `lk`
+  // while the direct loads into `nxt` are in flight.
+  auto tile = [&](int jt, const uint8_t* __restrict__ lk, uint8_t* __restrict__ nxt) {
+    if (jt + 1 < ntiles) issue_tile(jt + 1, nxt);
     const uint8_t* lv = lk + C::TILE_BYTES;
     const int key0 = jt * BN;
     const bool need_mask = key0 + BN > kfull;
@@ -312,6 +307,14 @@ __global__ __launch_bounds__((BwdCfg<D, dq_waves<D>()>::THREADS)) void bwd_dq_ke
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  // The barrier also waits for this wave's loads of tile jt (the compiler
+  // completes loads to LDS before a workgroup barrier), so after it every
+  // wave's part of tile jt is in LDS and no wave still reads the other stage.
+  for (int jt = 0; jt < ntiles; ++jt) {
+    bwd_wait_vmem();
+    __syncthreads();
+    tile(jt, lds + (jt & 1) * 2 * C::TILE_BYTES, lds + ((jt + 1) & 1) * 2 * C::TILE_BYTES);
   }
 
   // epilogue: lane holds dQ^T[d = 32 db + 8 (i/4) + 4 (lane/32) + i%4][row]
