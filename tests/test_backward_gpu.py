@@ -133,6 +133,42 @@ def test_backward_on_fused_buffers_equals_packed_bitwise():
     assert bool((g[:, Hq + 2 * Hkv:].view(torch.int16) == SENT).all())
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_with_the_widest_rows(D):
+    """Every tensor of the backward 2^24 - 8 elements per token row (32 MiB),
+    the widest the backward accepts: the kernels' 32-bit in-tile and in-step
+    byte offsets reach their largest values. Equal to the packed call bit for
+    bit, and the oracle."""
+    import varlen_gqa_attention_amd as V
+    Hq, Hkv = 4, 2
+    lens = [3, 2]
+    cu = I.cu_from_lengths(lens)
+    T = int(cu[-1])
+    rs = (1 << 24) - 8
+    print(f"[wide rows] backward D={D} stride={rs}", flush=True)
+    plan = V.Plan(len(lens), 8, 8, Hq, Hkv, D, True, backward=True)
+    q = I.normal_bf16((T, Hq, D), 70 + D, "cuda")
+    k = I.normal_bf16((T, Hkv, D), 71 + D, "cuda")
+    v = I.normal_bf16((T, Hkv, D), 72 + D, "cuda")
+    dout = I.normal_bf16((T, Hq, D), 73 + D, "cuda")
+    c = torch.from_numpy(cu).cuda()
+    out, lse = plan(q, k, v, c, c, B=len(lens))
+    dq0, dk0, dv0 = plan.backward(q, k, v, out, lse, dout, c, c, B=len(lens))
+
+    def wide(t):
+        store = torch.zeros((T - 1) * rs + t.shape[1] * D, dtype=torch.bfloat16, device="cuda")
+        w = store.as_strided(tuple(t.shape), (rs, D, 1))
+        w.copy_(t)
+        return w
+    qw, kw, vw, ow, dow = wide(q), wide(k), wide(v), wide(out), wide(dout)
+    dqw, dkw, dvw = wide(torch.zeros_like(q)), wide(torch.zeros_like(k)), wide(torch.zeros_like(v))
+    plan.backward(qw, kw, vw, ow, lse, dow, c, c, dq=dqw, dk=dkw, dv=dvw, B=len(lens))
+    torch.cuda.synchronize()
+    for a, b in ((dqw, dq0), (dkw, dk0), (dvw, dv0)):
+        assert torch.equal(a.contiguous().view(torch.int16), b.view(torch.int16))
+    _check(len(lens), cu, cu, q, k, v, dout, dq0, dk0, dv0, True, "wide rows")
+
+
 def test_backward_needs_a_backward_plan_and_valid_strides():
     import varlen_gqa_attention_amd as V
     from varlen_gqa_attention_amd import _lib
