@@ -21,7 +21,9 @@
 // reads run a few k-steps ahead of the MFMAs that consume them. The softmax
 // scale folds into the exponent's FMA; the running max used for the exponent
 // is only raised when a row's max grows by more than 2^8, so the O accumulator
-// is rescaled rarely (exact: l uses the same reference).
+// is rescaled rarely (exact: l uses the same reference), and once every row
+// of a wave has a reference a tile skips the row max unless its weights grew
+// past 2^30.
 // Only tiles that cross the causal diagonal or the end of the keys are masked.
 //
 // Workgroup order is XCD-aware: workgroup i runs on XCD i % 8, so the grid is
@@ -197,12 +199,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   // rounded to bf16 as they enter the P V product (normalises O, so the
   // output is a weighted mean of V rows with exactly the weights used)
   float m[RB], l[RB], lt[RB];
+  bool settled[RB];  // every row of the wave has a reference max (wave-uniform)
   f32x16 o[RB][DBLK];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m[rb] = kNegInf;
     l[rb] = 0.f;
     lt[rb] = 0.f;
+    settled[rb] = false;
 #pragma unroll
     for (int i = 0; i < DBLK; ++i)
 #pragma unroll
@@ -265,43 +269,63 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
             if (key > row_lim[rb] || key >= Lk) sacc[rb][kb][i] = kNegInf;
           }
       }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][kb][i]);
-      mx = max_xor32(mx) * a.c;   // row max in base-2 units
-      // raise the reference max only when the row max grew by more than 2^8
-      // (or the row had no reference yet); rescale O and l when it moves
-      const bool grow = mx > m[rb] + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float mnew = grow ? mx : m[rb];
-        const float alpha = fast_exp2(m[rb] - mnew);  // m = -inf -> 0
-        if (grow) {
-          m[rb] = mnew;
-          l[rb] *= alpha;
-          lt[rb] *= alpha;
-#pragma unroll
-          for (int i = 0; i < DBLK; ++i) o[rb][i] *= alpha;
-        }
-      }
-      const float msub = (m[rb] == kNegInf) ? 0.f : m[rb];
+      // P = exp2(S c - msub) rounded to bf16 into pk; psum / ptsum: the
+      // lane's sums of the fp32 and of the bf16-rounded weights
       float psum = 0.f, ptsum = 0.f;
+      auto exps = [&](float msub) __attribute__((always_inline)) {
+        psum = 0.f;
+        ptsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j], a.c, -msub));
-            const float p1 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j + 1], a.c, -msub));
-            psum += p0 + p1;
-            const uint32_t w2 = pack_bf16x2(p0, p1);
-            pk[rb][kb][h][j] = w2;
-            ptsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2),
-                                                    __builtin_bit_cast(bf16x2, 0x3F803F80u),
-                                                    ptsum, false);
+            for (int j = 0; j < 4; ++j) {
+              const float p0 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j], a.c, -msub));
+              const float p1 = fast_exp2(fmaf(sacc[rb][kb][8 * h + 2 * j + 1], a.c, -msub));
+              psum += p0 + p1;
+              const uint32_t w2 = pack_bf16x2(p0, p1);
+              pk[rb][kb][h][j] = w2;
+              ptsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2),
+                                                      __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                                      ptsum, false);
+            }
+      };
+      // Once every row of the wave has a reference, the tile's weights are
+      // taken against it without a row max; only if some weight may have
+      // grown past 2^30 (a lane's sum says so: the sum of 32 weights bounds
+      // each) is the tile redone with the max below. Weights up to 2^35 keep
+      // l, lt and O far from the fp32 range, and the reference cancels in O
+      // and in the LSE.
+      bool redo = true;
+      if (settled[rb]) {
+        exps(m[rb]);
+        redo = __builtin_amdgcn_ballot_w64(!(psum <= 0x1p30f)) != 0;
+      }
+      if (redo) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[rb][kb][i]);
+        mx = max_xor32(mx) * a.c;   // row max in base-2 units
+        // raise the reference max when the row max grew by more than 2^8
+        // (or the row had no reference yet); rescale O and l when it moves
+        const bool grow = mx > m[rb] + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float mnew = grow ? mx : m[rb];
+          const float alpha = fast_exp2(m[rb] - mnew);  // m = -inf -> 0
+          if (grow) {
+            m[rb] = mnew;
+            l[rb] *= alpha;
+            lt[rb] *= alpha;
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i) o[rb][i] *= alpha;
           }
+        }
+        exps((m[rb] == kNegInf) ? 0.f : m[rb]);
+        settled[rb] = __builtin_amdgcn_ballot_w64(m[rb] == kNegInf) == 0;
+      }
       l[rb] += psum;
       lt[rb] += ptsum;
     }
