@@ -136,6 +136,40 @@ def test_full_size_varlen_prefill_sampled():
     run_prefill(w, 0, picks=picks)
 
 
+@pytest.mark.parametrize("growth", [0.05, 0.5, 4.0])
+@pytest.mark.parametrize("D", [64, 128])
+def test_growing_scores(growth, D):
+    """Keys scaled up along each sequence (key j of a sequence by 1 + growth *
+    j / 64), so a row's max score climbs tile after tile: by a few base-2
+    units over the sequence (weights stay against the first reference), by
+    tens (weights past 2^8 but under 2^30, still no rescale), and by hundreds
+    (tiles redone with the row max and O rescaled). Against the oracle. V is
+    scaled by 1/4: a softmax this peaked puts nearly all weight on one key,
+    so |O| follows |v|, and for |O| in [2, 4) one bf16 rounding of the output
+    (up to 2^-7) plus the rounding of the dominant weight exceeds 1e-2 for any
+    kernel that rounds P to bf16."""
+    import varlen_gqa_attention_amd as V
+    lens = [300, 129, 64, 700]
+    w = _prefill_workload(f"growing scores x{growth}", 8, 2, D, lens, lens, True)
+    print(f"[prefill] growing scores growth={growth} D={D}", flush=True)
+    m = I.materialise(w, 5, "cuda")
+    cu = m["cu_kv_np"]
+    scale = torch.ones(m["k"].shape[0], device="cuda")
+    for b in range(len(lens)):
+        j = torch.arange(int(cu[b + 1] - cu[b]), device="cuda", dtype=torch.float32)
+        scale[int(cu[b]):int(cu[b + 1])] = 1.0 + growth * j / 64.0
+    k = (m["k"].float() * scale[:, None, None]).to(torch.bfloat16)
+    v = (m["v"].float() * 0.25).to(torch.bfloat16)
+    plan = V.Plan(w["B_max"], w["s_max_q"], w["s_max_kv"], w["Hq"], w["Hkv"], D, True)
+    out, lse = plan(m["q"], k, v, m["cu_q"], m["cu_kv"], B=w["B"])
+    torch.cuda.synchronize()
+    ref_o, ref_l, written = A.attend_varlen(I.bf16_to_f64(m["q"]), I.bf16_to_f64(k),
+                                            I.bf16_to_f64(v), m["cu_q_np"], cu, w["B"], True)
+    assert np.isfinite(ref_l[written]).all()
+    assert_out_close(I.bf16_to_f64(out)[written], ref_o[written], w["name"])
+    assert_lse_close(lse.cpu().numpy().astype(np.float64)[written], ref_l[written], w["name"])
+
+
 def test_exact_grid_and_both_planned_grids_agree_bitwise():
     import varlen_gqa_attention_amd as V
     w = _prefill_workload("exact grid", 32, 8, 128, [100, 1, 700, 64], [100, 1, 700, 64], True,
