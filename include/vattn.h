@@ -403,7 +403,10 @@ vattn_status vattn_execute_noalloc(int B_max, int s_max_q, int s_max_kv, int Hq,
                                    int64_t q_rows, int64_t kv_rows, int32_t* err_word,
                                    vattn_stream_t stream);
 
-/* Free the plan's scratch. Safe on NULL. Work already enqueued must be done. */
+/* Free the plan's scratch. Safe on NULL. Work already enqueued must be done.
+ * Calls hipFree: not to be called while any stream of the device is being
+ * captured in global mode (the capture would be invalidated); the Python
+ * binding defers a plan released during a capture of its current stream. */
 void vattn_plan_destroy(vattn_plan_t p);
 
 #ifdef __cplusplus

@@ -191,3 +191,30 @@ def test_backward_plan_limits(s_max_q, Hq, Hkv, D):
         V.describe_plan(2, s_max_q, 64, Hq, Hkv, D, 1, n_cu_override=256, backward=1)
     assert e.value.status == -2
     V.describe_plan(2, s_max_q, 64, Hq, Hkv, D, 1, n_cu_override=256)
+
+
+def test_plan_released_during_capture_is_freed_after_it(monkeypatch):
+    """A plan handle released while the current stream captures a graph is not
+    freed then (hipFree would invalidate a global-mode capture), but at the
+    next release outside a capture; nothing is freed twice."""
+    import varlen_gqa_attention_amd as V
+    freed = []
+
+    class FakeLib:
+        def vattn_plan_destroy(self, h):
+            freed.append(h)
+
+    monkeypatch.setattr(V, "_LIB", FakeLib())
+    monkeypatch.setattr(V, "_deferred_handles", [])
+    capturing = [True]
+    monkeypatch.setattr(V, "_capturing", lambda: capturing[0])
+    V._destroy_handle("a")
+    V._destroy_handle("b")
+    assert freed == [] and V._deferred_handles == ["a", "b"]
+    V._release_deferred()               # still capturing: nothing happens
+    assert freed == []
+    capturing[0] = False
+    V._destroy_handle("c")
+    assert sorted(freed) == ["a", "b", "c"] and V._deferred_handles == []
+    V._release_deferred()
+    assert sorted(freed) == ["a", "b", "c"]

@@ -199,3 +199,45 @@ def test_continuous_batching_hundred_steps_in_one_graph():
         assert_out_close(I.bf16_to_f64(outs[t]), ref_o, f"step {t}")
         assert_lse_close(lses[t].cpu().numpy(), ref_l, f"step {t}")
         print(f"[graph 100 steps] step {t} matches the oracle", flush=True)
+
+
+def test_plan_collected_inside_a_capture():
+    """A plan that only a reference cycle keeps alive, collected by the garbage
+    collector while a global-mode capture is open, must not free its scratch
+    inside the capture: the capture completes and replays correctly."""
+    import gc
+    import varlen_gqa_attention_amd as V
+    B, Hq, Hkv, D, smax = 4, 8, 2, 64, 256
+    lens = I.uniform_lengths(B, 1, smax, 5, 0)
+    cu_kv = torch.from_numpy(I.cu_from_lengths(lens)).cuda()
+    q = I.normal_bf16((B, Hq, D), 110, "cuda")
+    k = I.normal_bf16((B * smax, Hkv, D), 111, "cuda")
+    v = I.normal_bf16((B * smax, Hkv, D), 112, "cuda")
+    cu_q = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    plan = V.Plan(B, 1, smax, Hq, Hkv, D, False, force_nsplit=2)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(B, Hq, device="cuda")
+    plan(q, k, v, cu_q, cu_kv, out=out, lse=lse, B=B)   # warm-up outside capture
+    torch.cuda.synchronize()
+    gc.collect()
+    doomed = V.Plan(B, 1, smax, Hq, Hkv, D, False)
+    cycle = {"plan": doomed}
+    cycle["self"] = cycle
+    del doomed, cycle
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s, capture_error_mode="global"):
+        gc.collect()                    # the cycle's plan is released here
+        plan(q, k, v, cu_q, cu_kv, out=out, lse=lse, B=B)
+    torch.cuda.synchronize()
+    assert len(V._deferred_handles) == 1
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    o_e, l_e = plan(q, k, v, cu_q, cu_kv, B=B)
+    torch.cuda.synchronize()
+    assert torch.equal(o_e.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(l_e, lse)
+    V._release_deferred()
+    assert V._deferred_handles == []

@@ -76,11 +76,41 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+# Plan handles released while the current stream is capturing a graph. Freeing
+# a plan calls hipFree, which a global-mode capture forbids from every thread
+# (the capture would be invalidated); a plan dropped there, for instance by a
+# garbage-collector pass that runs inside the capture, is freed at the next
+# release or plan creation outside a capture instead.
+_deferred_handles = []
+
+
+def _capturing():
+    import torch
+    try:
+        return torch.cuda.is_current_stream_capturing()
+    except Exception:
+        return False
+
+
+def _release_deferred():
+    while _deferred_handles and not _capturing():
+        _LIB.vattn_plan_destroy(_deferred_handles.pop())
+
+
+def _destroy_handle(h):
+    if _capturing():
+        _deferred_handles.append(h)
+        return
+    _LIB.vattn_plan_destroy(h)
+    _release_deferred()
+
+
 class Plan:
     """A plan for up to B_max sequences (see vattn_plan in include/vattn.h)."""
 
     def __init__(self, B_max, s_max_q, s_max_kv, Hq, Hkv, D, causal=True, **opts):
         self._h = ctypes.c_void_p()
+        _release_deferred()
         o = _opts(**opts)
         _lib.check(_LIB.vattn_plan_ex(ctypes.byref(self._h), B_max, s_max_q, s_max_kv, Hq, Hkv,
                                       D, int(causal), ctypes.byref(o)), "vattn_plan")
@@ -240,7 +270,7 @@ class Plan:
 
     def close(self):
         if self._h:
-            _LIB.vattn_plan_destroy(self._h)
+            _destroy_handle(self._h)
             self._h = ctypes.c_void_p()
 
     def __del__(self):
