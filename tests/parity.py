@@ -21,7 +21,15 @@ these roundings (causal, L up to 2000, D 32 and 128, N(0,1) inputs) gives
 per-head element errors beyond the output rounding of at most 0.0094 and
 Frobenius ratios of 0.0021-0.0027; dk and dv add G independent per-head
 errors, which grow as sqrt(G) (emulated: 0.0068 at G = 1, 0.020 at G = 16),
-while the Frobenius ratio does not grow with G.
+while the Frobenius ratio does not grow with G. Where the oracle's gradient
+is zero everywhere the Frobenius ratio is 0/0; a result at the rounding level
+of fp32 sums (every |x| <= 2^-10) is then accepted: a gradient that vanishes
+by cancellation, e.g. dq and dk of a row whose only visible key has weight
+1 (dS = p (dP - delta) with dP = delta exactly), comes out as the difference
+of two fp32 sums of the same D bf16 products taken in different orders, at
+most 2 D 2^-24 sum|dO v| before the scale and |k| factors (below 1e-3 at
+D <= 256 for N(0,1) inputs). Rows that see no key are exactly zero by
+construction; `assert_zero_rows` checks that separately.
 """
 import numpy as np
 
@@ -32,6 +40,7 @@ LSE_ATOL = 1e-4
 GRAD_ATOL = 2e-2
 GRAD_RTOL = 2.0 ** -8
 GRAD_FRO = 1e-2
+GRAD_ZERO_ATOL = 2.0 ** -10  # all-zero reference: rounding level of fp32 sums
 
 
 def bf16_ulp(x):
@@ -87,5 +96,12 @@ def assert_grad_close(got, ref, what="", heads=1):
         fro = np.linalg.norm(got - ref) / nr
         assert fro <= GRAD_FRO, f"{what}: relative Frobenius error {fro:.3e}"
     else:
-        assert np.linalg.norm(got) == 0, f"{what}: nonzero gradient where the oracle has none"
+        assert (np.abs(got) <= GRAD_ZERO_ATOL).all(), \
+            f"{what}: gradient above rounding level where the oracle has none"
     return float(err.max()) if err.size else 0.0
+
+
+def assert_zero_rows(got, rows, what=""):
+    """Gradient rows that no visible key (or query) reaches are exactly 0."""
+    got = np.asarray(got, dtype=np.float64)
+    assert (got[rows] == 0).all(), f"{what}: nonzero gradient in rows no key reaches"

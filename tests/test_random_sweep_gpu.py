@@ -12,7 +12,7 @@ import torch
 
 from oracle import attention as A
 from oracle import backward as BW
-from tests.parity import assert_grad_close, assert_lse_close, assert_out_close
+from tests.parity import assert_grad_close, assert_lse_close, assert_out_close, assert_zero_rows
 from varlen_gqa_attention_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -63,13 +63,80 @@ def _case(seed):
                 fused=fused)
 
 
+SPECIAL_LARGE = [0, 1, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025]
+
+
+def _lengths_large(rng, B, hi):
+    out = []
+    for _ in range(B):
+        r = rng.random()
+        if r < 0.3:
+            out.append(min(hi, int(rng.choice(SPECIAL_LARGE))))
+        elif r < 0.4:
+            out.append(hi - int(rng.integers(0, 2)))
+        else:
+            out.append(int(rng.integers(0, hi + 1)))
+    return np.array(out, dtype=np.int64)
+
+
+def _case_large(seed):
+    """Longer sequences: decode over up to 9000 keys with split, path and
+    merge options, batches up to 40 in larger cu buffers; prefill over up to
+    1100 tokens (several query and key tiles, ragged ends), its backward on
+    about half of the cases."""
+    rng = np.random.default_rng([37, seed])
+    D = int(rng.choice([64, 128, 128, 256]))
+    decode = bool(rng.random() < 0.5)
+    causal = bool(rng.random() < 0.7)
+    opts = {}
+    if decode:
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 4, 8, 16, 32]))
+        B = int(rng.integers(1, 41))
+        B_max = B + int(rng.integers(0, 9))
+        s_max_kv = int(rng.choice([1000, 4096, 9000]))
+        s_max_q = 1
+        q_lens = np.ones(B, np.int64)
+        q_lens[rng.random(B) < 0.1] = 0
+        kv_lens = _lengths_large(rng, B, s_max_kv)
+        opts["force_nsplit"] = int(rng.choice([0, 0, 5, 16, 32]))
+        opts["force_decode_path"] = int(rng.choice([0, 0, 1, 2]))
+        opts["fuse_combine"] = int(rng.choice([0, 0, 1, 2]))
+        if opts["force_nsplit"] == 0 and rng.random() < 0.5:
+            opts["split_rule"] = "pages"
+    else:
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 4, 8, 16]))
+        B = int(rng.integers(1, 4))
+        B_max = B + int(rng.integers(0, 3))
+        s_max_q = int(rng.choice([600, 1100]))
+        s_max_kv = s_max_q
+        q_lens = _lengths_large(rng, B, s_max_q)
+        kv_lens = q_lens.copy() if rng.random() < 0.6 else _lengths_large(rng, B, s_max_kv)
+        opts["prefill_grid"] = int(rng.integers(0, 2))
+        if rng.random() < 0.5:
+            opts["backward"] = 1
+    fused = bool(rng.random() < 0.3)
+    return dict(D=D, Hkv=Hkv, Hq=Hkv * G, B=B, B_max=B_max, causal=causal, decode=decode,
+                s_max_q=s_max_q, s_max_kv=s_max_kv, q_lens=q_lens, kv_lens=kv_lens, opts=opts,
+                fused=fused)
+
+
 @pytest.mark.parametrize("seed", range(120))
 def test_random_configuration(seed):
+    _run(_case(seed), seed, "sweep")
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_configuration_large(seed):
+    _run(_case_large(seed), 500 + seed, "large sweep")
+
+
+def _run(c, seed, name):
     import varlen_gqa_attention_amd as V
-    c = _case(seed)
-    print(f"[sweep {seed}] D={c['D']} Hq={c['Hq']} Hkv={c['Hkv']} B={c['B']}/{c['B_max']} "
+    print(f"[{name} {seed}] D={c['D']} Hq={c['Hq']} Hkv={c['Hkv']} B={c['B']}/{c['B_max']} "
           f"decode={c['decode']} causal={c['causal']} fused={c['fused']} opts={c['opts']} "
-          f"q={c['q_lens'].tolist()} kv={c['kv_lens'].tolist()}", flush=True)
+          f"q={c['q_lens'].tolist()[:12]} kv={c['kv_lens'].tolist()[:12]}", flush=True)
     B, Hq, Hkv, D = c["B"], c["Hq"], c["Hkv"], c["D"]
     cu_q = I.cu_from_lengths(c["q_lens"], capacity=c["B_max"] + 1, tail=[-1, 2**31 - 1])
     cu_k = I.cu_from_lengths(c["kv_lens"], capacity=c["B_max"] + 1, tail=[-1, 2**31 - 1])
@@ -93,9 +160,9 @@ def test_random_configuration(seed):
     assert plan.read_error() == 0
     qf, kf, vf = I.bf16_to_f64(q), I.bf16_to_f64(k), I.bf16_to_f64(v)
     ro, rl, wr = A.attend_varlen(qf, kf, vf, cu_q, cu_k, B, c["causal"])
-    assert_out_close(I.bf16_to_f64(out)[wr], ro[wr], f"sweep {seed} out")
-    assert_lse_close(lse.cpu().numpy()[wr], rl[wr], f"sweep {seed} lse")
-    if c["decode"]:
+    assert_out_close(I.bf16_to_f64(out)[wr], ro[wr], f"{name} {seed} out")
+    assert_lse_close(lse.cpu().numpy()[wr], rl[wr], f"{name} {seed} lse")
+    if c["decode"] or not c["opts"].get("backward"):
         return
     dout = I.normal_bf16((Tq, Hq, D), 5000 + seed, "cuda")
     dq, dk, dv = (torch.zeros(t.shape, dtype=torch.bfloat16, device="cuda") for t in (q, k, v))
@@ -103,6 +170,8 @@ def test_random_configuration(seed):
     torch.cuda.synchronize()
     gq, gk, gv, wq, wk = BW.attend_varlen_backward(qf, kf, vf, I.bf16_to_f64(dout), cu_q, cu_k,
                                                    B, c["causal"])
-    assert_grad_close(I.bf16_to_f64(dq)[wq], gq[wq], f"sweep {seed} dq")
-    assert_grad_close(I.bf16_to_f64(dk)[wk], gk[wk], f"sweep {seed} dk", heads=Hq // Hkv)
-    assert_grad_close(I.bf16_to_f64(dv)[wk], gv[wk], f"sweep {seed} dv", heads=Hq // Hkv)
+    assert_grad_close(I.bf16_to_f64(dq)[wq], gq[wq], f"{name} {seed} dq")
+    # query rows that see no key (LSE = -inf) have dq exactly 0
+    assert_zero_rows(I.bf16_to_f64(dq), wr[:, None] & np.isneginf(rl), f"{name} {seed} dq")
+    assert_grad_close(I.bf16_to_f64(dk)[wk], gk[wk], f"{name} {seed} dk", heads=Hq // Hkv)
+    assert_grad_close(I.bf16_to_f64(dv)[wk], gv[wk], f"{name} {seed} dv", heads=Hq // Hkv)
