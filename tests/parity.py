@@ -11,9 +11,14 @@ inputs at D <= 256) is not relative to the tiny result. -inf must match
 exactly and NaN always fails.
 
 Gradients (bf16 dq, dk, dv) against the unrounded fp64 oracle: every element
-within 2e-2 * sqrt(n) + 2^-8 |ref|, where n is the number of query heads
-whose contributions the element sums (1 for dq, G for dk and dv), and the
-whole tensor within 1e-2 relative in the Frobenius norm. Derivation: the
+within 2e-2 * sqrt(n) * max(1, rms(ref)) + 2^-8 |ref|, where n is the number
+of query heads whose contributions the element sums (1 for dq, G for dk and
+dv) and rms(ref) the root mean square of the reference tensor, and the whole
+tensor within 1e-2 relative in the Frobenius norm. The rms factor is 1 on
+the long causal sequences the derivation below emulates; few keys seen by
+many queries give gradients of rms well above 1, whose rounding errors grow
+in proportion (emulated in tests/test_grad_tolerance_derivation.py: the
+unscaled term fails there, the scaled one holds with a 1.25x margin). Derivation: the
 kernels round the softmax weights and dS to bf16 as MFMA operands (2^-9
 relative each, random), take <dO, O> from the forward's bf16 output, and
 round the results to bf16 (the 2^-8 |ref| term); an fp64 emulation of exactly
@@ -79,13 +84,19 @@ def assert_lse_close(got, ref, what=""):
     return float(err.max()) if err.size else 0.0
 
 
+def grad_scale(ref):
+    """max(1, root mean square of the reference gradient tensor)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    return max(1.0, float(np.sqrt(np.mean(ref ** 2)))) if ref.size else 1.0
+
+
 def assert_grad_close(got, ref, what="", heads=1):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert not np.isnan(got).any(), f"{what}: NaN in gradient"
     err = np.abs(got - ref)
-    bad = err > GRAD_ATOL * np.sqrt(heads) + GRAD_RTOL * np.abs(ref)
+    bad = err > GRAD_ATOL * np.sqrt(heads) * grad_scale(ref) + GRAD_RTOL * np.abs(ref)
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} gradients out of tolerance; max err "

@@ -29,7 +29,7 @@ import pytest
 from oracle import attention as A
 from oracle import backward as BW
 from oracle.bf16 import round_bf16
-from tests.parity import GRAD_ATOL, GRAD_FRO, GRAD_RTOL
+from tests.parity import GRAD_ATOL, GRAD_FRO, GRAD_RTOL, grad_scale
 
 
 def emulated_backward_rows(qh, kh, vh, doh, out_bf16, lse, visible, scale):
@@ -44,6 +44,28 @@ def emulated_backward_rows(qh, kh, vh, doh, out_bf16, lse, visible, scale):
     delta = (doh * out_bf16).sum(axis=1)
     ds = round_bf16(p * (dp - delta[:, None]))
     return scale * (ds @ kh), scale * (ds.T @ qh), dv
+
+
+def few_key_errors(Lq, Lk, D, seed):
+    """One non-causal sequence of Lq queries over Lk keys, one head: the
+    largest ratio, per gradient, of the emulated element error (bf16-stored,
+    beyond the GRAD_RTOL rounding term) to the bound's absolute term, with
+    and without its scaling by the gradient's RMS."""
+    rng = np.random.default_rng([97, Lq, Lk, D, seed])
+    bf = lambda *shape: round_bf16(rng.standard_normal(shape))
+    q, k, v, do = bf(Lq, 1, D), bf(Lk, 1, D), bf(Lk, 1, D), bf(Lq, 1, D)
+    cq, ck = np.array([0, Lq]), np.array([0, Lk])
+    out, lse, _ = A.attend_varlen(q, k, v, cq, ck, 1, False)
+    refs = BW.attend_varlen_backward(q, k, v, do, cq, ck, 1, False)[:3]
+    emu = emulated_backward_rows(q[:, 0], k[:, 0], v[:, 0], do[:, 0], round_bf16(out[:, 0]),
+                                 lse[:, 0], A.visible_keys(Lq, Lk, False), 1.0 / np.sqrt(D))
+    res = {}
+    for name, got, ref in zip(("dq", "dk", "dv"), emu, refs):
+        ref = ref[:, 0]
+        err = np.abs(round_bf16(got) - ref) - GRAD_RTOL * np.abs(ref)
+        res[name] = (float(err.max() / (GRAD_ATOL * grad_scale(ref))),
+                     float(err.max() / GRAD_ATOL))
+    return res
 
 
 def one_sequence_errors(L, D, G, seed, causal=True):
@@ -100,3 +122,18 @@ def test_gradient_bound_follows_from_the_roundings(D):
     # (its maximum still rises a little with G, being taken over G times as
     # many elements)
     assert worst[(16, "dq")][0] * 1.5 <= GRAD_ATOL
+
+
+def test_bound_scales_with_the_gradient_rms():
+    """Few keys seen by many queries (non-causal) give dk and dv of RMS
+    well above 1 (sums of many terms of weight about 1 / Lk), and rounding
+    errors in proportion: there the unscaled absolute bound of 2e-2 fails
+    (by up to 4.5x) while 2e-2 max(1, rms) holds with a 1.25x margin (dk and
+    dv use under 0.4 of it; dq, whose RMS stays below 1, up to 0.7)."""
+    unscaled = 0.0
+    for Lq, Lk, D in ((451, 4, 256), (1000, 2, 64), (2000, 8, 128)):
+        for seed in range(2):
+            for name, (scaled, plain) in few_key_errors(Lq, Lk, D, seed).items():
+                assert scaled * 1.25 <= 1.0, (Lq, Lk, D, name, scaled)
+                unscaled = max(unscaled, plain)
+    assert unscaled > 1.0
