@@ -122,6 +122,74 @@ def _case_large(seed):
                 fused=fused)
 
 
+def _case_edge(seed):
+    """Shapes at the edges of the method: few query tokens against long keys
+    (speculative-decoding rows), large G folded into few-token tiles, many
+    tiny sequences in a large batch buffer (rows that see one to a few keys,
+    where the weights' bf16 rounding matters most), and MHA with unequal
+    non-causal lengths (few keys seen by many queries)."""
+    rng = np.random.default_rng([41, seed])
+    kind = int(rng.integers(0, 4))
+    D = int(rng.choice([32, 64, 128, 256]))
+    causal = bool(rng.random() < 0.7)
+    opts = {}
+    if kind == 0:
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 4, 8, 16]))
+        B = int(rng.integers(1, 17))
+        B_max = B + int(rng.integers(0, 5))
+        s_max_q = int(rng.choice([2, 4, 8]))
+        s_max_kv = int(rng.choice([500, 3000]))
+        q_lens = rng.integers(0, s_max_q + 1, B).astype(np.int64)
+        kv_lens = _lengths_large(rng, B, s_max_kv)
+        opts["prefill_grid"] = int(rng.integers(0, 2))
+        opts["backward"] = int(rng.random() < 0.5)
+    elif kind == 1:
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([32, 64, 128] if D <= 128 else [32, 64]))
+        B = int(rng.integers(1, 4))
+        B_max = B
+        s_max_q = int(rng.choice([40, 130]))
+        s_max_kv = s_max_q
+        q_lens = _lengths(rng, B, s_max_q)
+        kv_lens = q_lens.copy()
+        opts["prefill_grid"] = int(rng.integers(0, 2))
+        opts["backward"] = int(rng.random() < 0.3)
+    elif kind == 2:
+        Hkv = int(rng.choice([1, 4, 8]))
+        G = int(rng.choice([1, 2, 8]))
+        B = int(rng.integers(50, 257))
+        B_max = B + int(rng.integers(0, 64))
+        decode = bool(rng.random() < 0.5)
+        s_max_kv = int(rng.choice([20, 70]))
+        if decode:
+            s_max_q = 1
+            q_lens = np.ones(B, np.int64)
+            q_lens[rng.random(B) < 0.1] = 0
+            kv_lens = _lengths(rng, B, s_max_kv)
+            opts["force_nsplit"] = int(rng.choice([0, 2]))
+        else:
+            s_max_q = s_max_kv
+            q_lens = _lengths(rng, B, s_max_q)
+            kv_lens = q_lens.copy()
+            opts["prefill_grid"] = int(rng.integers(0, 2))
+            opts["backward"] = int(rng.random() < 0.5)
+    else:
+        Hkv = int(rng.choice([4, 8]))
+        G = 1
+        B = int(rng.integers(1, 5))
+        B_max = B
+        s_max_q = int(rng.choice([300, 700]))
+        s_max_kv = int(rng.choice([300, 900]))
+        q_lens = _lengths_large(rng, B, s_max_q)
+        kv_lens = _lengths_large(rng, B, s_max_kv)
+        opts["prefill_grid"] = int(rng.integers(0, 2))
+        opts["backward"] = 1
+    return dict(D=D, Hkv=Hkv, Hq=Hkv * G, B=B, B_max=B_max, causal=causal, decode=s_max_q == 1,
+                s_max_q=s_max_q, s_max_kv=s_max_kv, q_lens=q_lens, kv_lens=kv_lens, opts=opts,
+                fused=bool(rng.random() < 0.3))
+
+
 @pytest.mark.parametrize("seed", range(120))
 def test_random_configuration(seed):
     _run(_case(seed), seed, "sweep")
@@ -130,6 +198,13 @@ def test_random_configuration(seed):
 @pytest.mark.parametrize("seed", range(32))
 def test_random_configuration_large(seed):
     _run(_case_large(seed), 500 + seed, "large sweep")
+
+
+# seeds 52 ... 285 had outputs or gradients past the bounds before the
+# weights' remainder term and the gradient-rms scaling of the bound
+@pytest.mark.parametrize("seed", list(range(40)) + [52, 94, 104, 117, 153, 169, 285])
+def test_random_configuration_edge(seed):
+    _run(_case_edge(seed), 900 + seed, "edge sweep")
 
 
 def _run(c, seed, name):

@@ -447,7 +447,8 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 2 : 1) void decode_mfma_kernel(
     fetch_rows(t + 2 * NW, r);
   };
 
-  auto process_tile = [&](int t, const u32x4 (&kr)[KB][KS], const u32x4 (&vr)[DV]) {
+  auto process_tile = [&](int t, const u32x4 (&kr)[KB][KS], const u32x4 (&vr)[DV], auto lo_tag) {
+    constexpr bool lo = decltype(lo_tag)::value;
     const int key0 = kbeg + t * TILE;
     // stage V (row-major [key][d], swizzled) in this wave's LDS slice
 #pragma unroll
@@ -493,13 +494,27 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 2 : 1) void decode_mfma_kernel(
     m = mnew;
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[i] *= alpha;
-    uint32_t pw[2 * KB];
-#pragma unroll
-    for (int j = 0; j < 2 * KB; ++j) pw[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+    // For sequences of fewer than 256 keys (lo) P enters P V as two bf16
+    // operands, its rounding and the remainder p - bf16(p) rounded again (one
+    // more MFMA per d block), so the weights are exact to about 2^-17: with
+    // bf16 weights alone, a row whose few comparable weights multiply V rows
+    // far apart misses the output's rounding by up to 2^-8 max|v - O|; over
+    // more keys the weights' rounding errors average out.
+    uint32_t pw[2 * KB], pwl[2 * KB];
     float ptsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 2 * KB; ++j)
+    for (int j = 0; j < 2 * KB; ++j) {
+      pw[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
       ptsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[j]), as_bf16x2(kBf16One2), ptsum, false);
+    }
+    if constexpr (lo) {
+#pragma unroll
+      for (int j = 0; j < 2 * KB; ++j) {
+        pwl[j] = pack_bf16x2(p[2 * j] - bf16_lo(pw[j]), p[2 * j + 1] - bf16_hi(pw[j]));
+        ptsum =
+            __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pwl[j]), as_bf16x2(kBf16One2), ptsum, false);
+      }
+    }
     lt = lt * alpha + ptsum;
 
     wave_lds_sync();
@@ -516,12 +531,18 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 2 : 1) void decode_mfma_kernel(
         const bf16x4 x2 = lds_read_tr(vst + r2 * D * 2 + swz_tr16<D>(r2, ch) * 16 + half * 8);
         const bf16x8 vt = __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 pt = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        const bf16x8 ptl = __builtin_bit_cast(bf16x8, u32x4{pwl[0], pwl[1], pwl[2], pwl[3]});
         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pt, o[db], 0, 0, 0);
+        if constexpr (lo) o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, ptl, o[db], 0, 0, 0);
       } else {
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         const s16x4 pt = __builtin_bit_cast(s16x4, u32x2{pw[0], pw[1]});
+        const s16x4 ptl = __builtin_bit_cast(s16x4, u32x2{pwl[0], pwl[1]});
         o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, x1), pt, o[db],
                                                          0, 0, 0);
+        if constexpr (lo)
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, x1), ptl,
+                                                           o[db], 0, 0, 0);
       }
     }
     wave_lds_sync();
@@ -531,8 +552,18 @@ __global__ __launch_bounds__(NW * 64, D == 128 ? 2 : 1) void decode_mfma_kernel(
     fetch_rows(w, A);
     fetch_rows(w + (w + NW < ntiles ? NW : 0), B);
   }
-  pipeline_tiles<NW>(w, ntiles, A, B, [&](int t, TileRegs& r) { load_tile(t, r); },
-                     [&](int t, TileRegs& r) { process_tile(t, r.k, r.v); });
+  // sequences of fewer than 256 keys take P V with the remainder of P (see
+  // process_tile); each form is its own copy of the tile loop
+  if (Lk < 256)
+    pipeline_tiles<NW>(w, ntiles, A, B, [&](int t, TileRegs& r) { load_tile(t, r); },
+                       [&](int t, TileRegs& r) {
+                         process_tile(t, r.k, r.v, std::integral_constant<bool, true>{});
+                       });
+  else
+    pipeline_tiles<NW>(w, ntiles, A, B, [&](int t, TileRegs& r) { load_tile(t, r); },
+                       [&](int t, TileRegs& r) {
+                         process_tile(t, r.k, r.v, std::integral_constant<bool, false>{});
+                       });
   if constexpr (GATHER) report(a.err, gflags);
   // l: each lane summed its own 8 keys per tile; add the four key groups
   l = sum_xor32(sum_xor16(l));

@@ -214,9 +214,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   }
 
   // The two halves of tile jt: h1 = S^T = K Q^T + online softmax (leaves
-  // bf16 P in pk), h2 = O^T += V^T P^T.
-  u32x4 pk[RB][2][2];
-  auto h1 = [&](int jt, const uint8_t* lk) {
+  // bf16 P in pk), h2 = O^T += V^T P^T. With `lo` (the first key tile, when
+  // some row of the query tile sees fewer than 64 keys: then all of that
+  // row's keys are in it) P enters P V as two bf16 operands, its rounding pk
+  // and the remainder p - bf16(p) in pkl, one more MFMA per step: with bf16
+  // weights alone, a row whose few comparable weights multiply V rows far
+  // apart misses the output's rounding by up to 2^-8 max|v - O|; over 64 or
+  // more keys the weights' rounding errors average out.
+  u32x4 pk[RB][2][2], pkl[RB][2][2];
+  auto h1 = [&](int jt, const uint8_t* lk, bool lo) {
     const int key0 = jt * BN;
     // ---- S^T = K Q^T: two 32-key blocks x RB row blocks (K read once)
     f32x16 sacc[RB][2];
@@ -289,6 +295,13 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
               ptsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2),
                                                       __builtin_bit_cast(bf16x2, 0x3F803F80u),
                                                       ptsum, false);
+              if (lo) {
+                const uint32_t r2 = pack_bf16x2(p0 - bf16_lo(w2), p1 - bf16_hi(w2));
+                pkl[rb][kb][h][j] = r2;
+                ptsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, r2),
+                                                        __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                                        ptsum, false);
+              }
             }
       };
       // Once every row of the wave has a reference, the tile's weights are
@@ -331,7 +344,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
     }
 
   };
-  auto h2 = [&](const uint8_t* lv) {
+  auto h2 = [&](const uint8_t* lv, bool lo) {
     // ---- O^T += V^T P^T: k-steps (kb, h) of 16 keys; V^T read once for all
     //      row blocks
     // V^T fragments for the 4 k-steps (kb, h) stream from LDS one k-step
@@ -359,10 +372,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb) {
           o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               vt[step][db], __builtin_bit_cast(bf16x8, pk[rb][step >> 1][step & 1]), o[rb][db],
               0, 0, 0);
+          if (lo)
+            o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                vt[step][db], __builtin_bit_cast(bf16x8, pkl[rb][step >> 1][step & 1]),
+                o[rb][db], 0, 0, 0);
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -370,19 +388,25 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, uint8_t* lds,
   // One tile: issue tile jt + 1 into the other stage, then compute tile jt.
   // The stages are disjoint (restrict), which lets the compiler read `cur`
   // while the direct loads into `nxt` are in flight.
-  auto tile = [&](int jt, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+  auto tile = [&](int jt, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bool lo) {
     if (jt + 1 < ntiles) issue_tile(jt + 1, nxt);
-    h1(jt, cur);
-    h2(cur + C::TILE_BYTES);
+    h1(jt, cur, lo);
+    h2(cur + C::TILE_BYTES, lo);
   };
   // The barrier also waits for this wave's loads of tile jt (the compiler
   // completes direct-to-LDS loads before a workgroup barrier), so after it
   // every wave's part of tile jt is in LDS and no wave still reads the stage
-  // that tile jt + 1 goes to.
-  for (int jt = 0; jt < ntiles; ++jt) {
+  // that tile jt + 1 goes to. The first tile runs outside the loop, the only
+  // one that may take the remainder of P, so the loop's code is without it.
+  if (ntiles > 0) {
     wait_vmem_all();
     __syncthreads();
-    tile(jt, lds + (jt & 1) * 2 * C::TILE_BYTES, lds + ((jt + 1) & 1) * 2 * C::TILE_BYTES);
+    tile(0, lds, lds + 2 * C::TILE_BYTES, kfull < BN);
+  }
+  for (int jt = 1; jt < ntiles; ++jt) {
+    wait_vmem_all();
+    __syncthreads();
+    tile(jt, lds + (jt & 1) * 2 * C::TILE_BYTES, lds + ((jt + 1) & 1) * 2 * C::TILE_BYTES, false);
   }
 
   // ---- epilogue: lane holds O^T[d = 32 db + 8 (i/4) + 4 (lane>>5) + i%4][row]
