@@ -25,6 +25,9 @@
 // of a wave has a reference a tile skips the row max unless its weights grew
 // past 2^30.
 // Only tiles that cross the causal diagonal or the end of the keys are masked.
+// When a row of the query tile sees fewer than 64 keys (all of them in the
+// first key tile), that tile takes P V with P split into its bf16 rounding
+// and the bf16 remainder, so such rows' weights are not rounded to 8 bits.
 //
 // Workgroup order is XCD-aware: workgroup i runs on XCD i % 8, so the grid is
 // arranged such that each XCD walks whole (sequence, KV head) units, largest
